@@ -1,0 +1,247 @@
+"""Python binding of libdg.so: fine-grained-scaled FP8 E4M3 NT GEMM for MI355X.
+
+Argument marshalling only.  Each function has the name of the C entry point it
+calls (see ``include/dg.h`` for the operation, layouts and error behaviour),
+takes torch tensors that already live on the GPU, passes their device pointers
+and torch's current HIP stream, and raises :class:`DGError` on a non-zero
+status.  All arithmetic runs in the library's gfx950 kernels; there is no other
+implementation here and no fallback: if ``libdg.so`` is missing the import of
+the library fails with an error.
+
+Tensor conventions (the README's NT format and layouts):
+  A  ``torch.float8_e4m3fn`` (or uint8 holding E4M3 bytes), [M, K] contiguous rows
+  sA ``torch.float32`` [K/128, ld_sa] (MN-major: one row per K block)
+  B  E4M3 [N, K]; grouped [G, N, K]
+  sB ``torch.float32`` [ceil(N/128), K/128]; grouped [G, ceil(N/128), K/128]
+  D  ``torch.bfloat16`` (or int16/uint16 bits) [M, N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdg.so")
+
+DG_OK = 0
+DG_ERR_INVALID_ARG = -1
+DG_ERR_UNSUPPORTED = -2
+DG_ERR_MISALIGNED = -3
+DG_ERR_HIP = -4
+
+_lib = None
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdg.so (built by ``fp8_block_scaled_e4m3_amd.build``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libdg.so not found at {path}; run `python -m fp8_block_scaled_e4m3_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    P, L, I = ctypes.c_void_p, ctypes.c_long, ctypes.c_int
+    lib.dg_status_string.argtypes = [I]
+    lib.dg_status_string.restype = ctypes.c_char_p
+    lib.dg_get_m_alignment.argtypes = []
+    lib.dg_get_m_alignment.restype = I
+    lib.dg_set_num_cus.argtypes = [I]
+    lib.dg_set_num_cus.restype = I
+    lib.dg_get_num_cus.argtypes = []
+    lib.dg_get_num_cus.restype = I
+    lib.dg_gemm_fp8_nt.argtypes = [P, L, P, L, P, L, P, P, L, I, I, I, P]
+    lib.dg_gemm_fp8_nt.restype = I
+    lib.dg_m_grouped_gemm_fp8_contiguous.argtypes = [P, P, L, P, P, P, P, I, I, I, I, P]
+    lib.dg_m_grouped_gemm_fp8_contiguous.restype = I
+    lib.dg_m_grouped_gemm_fp8_masked.argtypes = [P, P, L, P, P, P, P, I, I, I, I, P]
+    lib.dg_m_grouped_gemm_fp8_masked.restype = I
+    lib.dg_set_kernel_config.argtypes = [I]
+    lib.dg_set_kernel_config.restype = I
+    lib.dg_kernel_config_info.argtypes = [I, P]
+    lib.dg_kernel_config_info.restype = I
+    lib.dg_plan_tiles.argtypes = [I, I, I, I, P, I, P, I, P, P]
+    lib.dg_plan_tiles.restype = I
+    lib.dg_describe_launch.argtypes = [I, I, I, I, I, I, P]
+    lib.dg_describe_launch.restype = I
+    _lib = lib
+    return lib
+
+
+def dg_status_string(status: int) -> str:
+    return load_library().dg_status_string(int(status)).decode()
+
+
+status_string = dg_status_string
+
+
+def _check(status: int, where: str) -> None:
+    if status != DG_OK:
+        raise DGError(status, where)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t, name: str, dtypes, ndim: int):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _fp8_types():
+    import torch
+    return (torch.float8_e4m3fn, torch.uint8)
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _bf16_types():
+    import torch
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def dg_get_m_alignment() -> int:
+    return int(load_library().dg_get_m_alignment())
+
+
+def dg_set_num_cus(n: int) -> None:
+    _check(load_library().dg_set_num_cus(int(n)), "dg_set_num_cus")
+
+
+def dg_get_num_cus() -> int:
+    v = int(load_library().dg_get_num_cus())
+    if v < 0:
+        raise DGError(v, "dg_get_num_cus")
+    return v
+
+
+def dg_gemm_fp8_nt(a, sa, b, sb, d, stream=None) -> None:
+    """D[m, n] = bf16(sum_kb sA[kb, m] * sB[n // 128, kb] * A[m, kb-block] . B[n, kb-block])."""
+    m, k = a.shape
+    n = b.shape[0]
+    pa = _dev(a, "a", _fp8_types(), 2)
+    psa = _dev(sa, "sa", _f32(), 2)
+    pb = _dev(b, "b", _fp8_types(), 2)
+    psb = _dev(sb, "sb", _f32(), 2)
+    pd = _dev(d, "d", _bf16_types(), 2)
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, d {tuple(d.shape)}")
+    if sa.shape[0] != -(-k // 128) or sb.shape[1] != -(-k // 128) or sb.shape[0] != -(-n // 128):
+        raise ValueError(f"scale shape mismatch: sa {tuple(sa.shape)}, sb {tuple(sb.shape)}")
+    if not sb.is_contiguous():
+        raise ValueError("sb must be contiguous")
+    _check(load_library().dg_gemm_fp8_nt(pa, a.stride(0), psa, sa.stride(0), pb, b.stride(0), psb,
+                                         pd, d.stride(0), m, n, k, _stream(stream)), "dg_gemm_fp8_nt")
+
+
+def dg_m_grouped_gemm_fp8_contiguous(a, sa, b, sb, d, m_indices, stream=None) -> None:
+    """Contiguous M-grouped GEMM; rows with m_indices == -1 are not written."""
+    import torch
+    m_total, k = a.shape
+    g, n, _ = b.shape
+    pa = _dev(a, "a", _fp8_types(), 2)
+    psa = _dev(sa, "sa", _f32(), 2)
+    pb = _dev(b, "b", _fp8_types(), 3)
+    psb = _dev(sb, "sb", _f32(), 3)
+    pd = _dev(d, "d", _bf16_types(), 2)
+    pmi = _dev(m_indices, "m_indices", (torch.int32,), 1)
+    for t, nm in ((a, "a"), (b, "b"), (sb, "sb"), (d, "d"), (m_indices, "m_indices")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if tuple(d.shape) != (m_total, n) or b.shape[2] != k or m_indices.shape[0] != m_total:
+        raise ValueError("shape mismatch")
+    if tuple(sb.shape) != (g, -(-n // 128), -(-k // 128)) or sa.shape[0] != -(-k // 128):
+        raise ValueError("scale shape mismatch")
+    _check(load_library().dg_m_grouped_gemm_fp8_contiguous(pa, psa, sa.stride(0), pb, psb, pd, pmi,
+                                                           m_total, n, k, g, _stream(stream)),
+           "dg_m_grouped_gemm_fp8_contiguous")
+
+
+def dg_m_grouped_gemm_fp8_masked(a, sa, b, sb, d, masked_m, stream=None) -> None:
+    """Masked M-grouped GEMM; rows >= masked_m[g] of d are never written."""
+    import torch
+    g, max_m, k = a.shape
+    n = b.shape[1]
+    pa = _dev(a, "a", _fp8_types(), 3)
+    psa = _dev(sa, "sa", _f32(), 3)
+    pb = _dev(b, "b", _fp8_types(), 3)
+    psb = _dev(sb, "sb", _f32(), 3)
+    pd = _dev(d, "d", _bf16_types(), 3)
+    pmm = _dev(masked_m, "masked_m", (torch.int32,), 1)
+    for t, nm in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb"), (d, "d"), (masked_m, "masked_m")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if tuple(b.shape) != (g, n, k) or tuple(d.shape) != (g, max_m, n) or masked_m.shape[0] != g:
+        raise ValueError("shape mismatch")
+    if tuple(sb.shape) != (g, -(-n // 128), -(-k // 128)) or sa.shape[:2] != (g, -(-k // 128)):
+        raise ValueError("scale shape mismatch")
+    _check(load_library().dg_m_grouped_gemm_fp8_masked(pa, psa, sa.shape[2], pb, psb, pd, pmm,
+                                                       g, max_m, n, k, _stream(stream)),
+           "dg_m_grouped_gemm_fp8_masked")
+
+
+def dg_set_kernel_config(config_id: int) -> None:
+    """Pin a kernel configuration id for its layout (-1: automatic planning again)."""
+    _check(load_library().dg_set_kernel_config(int(config_id)), "dg_set_kernel_config")
+
+
+def dg_kernel_config_info() -> list:
+    """All compiled kernel configurations as dicts (id, layout, block_m, block_n, waves)."""
+    out, res, i = (ctypes.c_int * 5)(), [], 0
+    while load_library().dg_kernel_config_info(i, out) == DG_OK:
+        res.append(dict(zip(("id", "layout", "block_m", "block_n", "waves"), list(out))))
+        i += 1
+    return res
+
+
+def dg_plan_tiles(m: int, n: int, num_units: int, block_ms, block_ns, eff=None, blocks_per_unit: int = 1):
+    """Host-only planner; returns (index, block_m, block_n, tiles, waves)."""
+    bm = (ctypes.c_int * len(block_ms))(*block_ms)
+    bn = (ctypes.c_int * len(block_ns))(*block_ns)
+    e = None if eff is None else (ctypes.c_double * len(eff))(*eff)
+    out = (ctypes.c_int * 4)()
+    r = load_library().dg_plan_tiles(m, n, num_units, blocks_per_unit, bm, len(block_ms), bn, len(block_ns),
+                                     e, out)
+    if r < 0:
+        raise DGError(r, "dg_plan_tiles")
+    return r, out[0], out[1], out[2], out[3]
+
+
+def dg_describe_launch(layout: int, m: int, n: int, k: int, num_groups: int = 1, num_cus: int = 0) -> dict:
+    """The launch a call of these sizes would make (layout 0 dense, 1 contiguous, 2 masked)."""
+    out = (ctypes.c_int * 6)()
+    r = load_library().dg_describe_launch(layout, m, n, k, num_groups, num_cus, out)
+    _check(r, "dg_describe_launch")
+    keys = ("block_m", "block_n", "waves_per_workgroup", "tiles", "grid", "config_id")
+    return dict(zip(keys, list(out)))
+
+
+__all__ = [
+    "DGError", "load_library", "status_string", "dg_status_string",
+    "dg_get_m_alignment", "dg_set_num_cus", "dg_get_num_cus",
+    "dg_gemm_fp8_nt", "dg_m_grouped_gemm_fp8_contiguous", "dg_m_grouped_gemm_fp8_masked",
+    "dg_set_kernel_config", "dg_kernel_config_info", "dg_plan_tiles", "dg_describe_launch",
+]

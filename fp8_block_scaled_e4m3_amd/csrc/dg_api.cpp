@@ -1,0 +1,399 @@
+// dg_api.cpp -- C ABI of libdg.so: argument validation, tile planning and
+// launch of the gfx950 kernels in dg_gemm.hip.  Host code only; it never
+// touches device memory (no allocation, copy, read-back or synchronisation), so
+// every entry point is asynchronous on the caller's stream and graph-capturable.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+
+#include "../../include/dg.h"
+#include "dg_internal.h"
+
+namespace {
+
+using dg::GemmParams;
+using dg::KernelConfig;
+
+constexpr int kKBlock = 128;
+constexpr int kMAlign = 128;           // contiguous-layout segment alignment
+constexpr int kMaxMaskedGroups = 1024; // LDS prefix table size in the masked kernel
+constexpr int kXcds = 8;
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_cu_cap{0};
+std::atomic<int> g_forced_cfg[3] = {{-1}, {-1}, {-1}};   // per layout: index into the table
+
+struct DeviceInfo {
+    bool init = false;
+    int cus = 0;
+    int occ[64] = {0};   // blocks per CU, indexed by position in the config table
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+bool debug_enabled() {
+    static int v = -1;
+    if (v < 0) {
+        const char* e = std::getenv("DG_DEBUG");
+        v = (e && e[0] && e[0] != '0') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+// Returns nullptr when no device is usable.
+const DeviceInfo* device_info(int* status) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        *status = DG_ERR_HIP;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.init) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+            (void)hipGetLastError();
+            *status = DG_ERR_HIP;
+            return nullptr;
+        }
+        int count = 0;
+        const KernelConfig* cfgs = dg::kernel_configs(&count);
+        for (int i = 0; i < count && i < 64; ++i) {
+            int blocks = 0;
+            if (cfgs[i].occupancy(&blocks) != hipSuccess || blocks <= 0) {
+                (void)hipGetLastError();
+                blocks = 1;
+            }
+            d.occ[i] = blocks;
+        }
+        d.cus = cus;
+        d.init = true;
+    }
+    *status = DG_OK;
+    return &d;
+}
+
+int effective_cus(int device_cus) {
+    const int cap = g_cu_cap.load();
+    return (cap > 0 && cap < device_cus) ? cap : device_cus;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
+// Planner order: the smaller estimated makespan (waves x per-tile work); on a tie
+// the plan with fewer waves, i.e. whole waves of larger tiles.
+bool better(double cost, long waves, double best_cost, long best_waves) {
+    const double tol = 1e-9 * (cost > best_cost ? cost : best_cost);
+    if (cost < best_cost - tol) return true;
+    if (cost > best_cost + tol) return false;
+    return waves < best_waves;
+}
+
+// Pick among the compiled configurations of one layout.
+int choose_config(int layout, int m, int n, int num_units, const DeviceInfo* dev, int max_m_hint) {
+    int count = 0;
+    const KernelConfig* cfgs = dg::kernel_configs(&count);
+    const int forced = g_forced_cfg[layout].load();
+    if (forced >= 0 && forced < count) return forced;
+    int best = -1;
+    double best_cost = 0.0;
+    long best_waves = 0;
+    for (int i = 0; i < count; ++i) {
+        const KernelConfig& c = cfgs[i];
+        if (c.layout != layout) continue;
+        if (layout == dg::kMasked) {
+            // the whole capacity in one row block when it fits, else the largest block
+            const int want = max_m_hint <= 128 ? 128 : 256;
+            if (c.bm != want) continue;
+            return i;
+        }
+        const int per_cu = dev ? dev->occ[i] : 1;
+        const long tiles = ceil_div(m, c.bm) * ceil_div(n, c.bn);
+        const long slots = (long)num_units * per_cu;
+        const long waves = ceil_div(tiles, slots);
+        // per-CU work of one wave of tiles; several resident blocks share one CU
+        const double cost = (double)waves * c.bm * c.bn * per_cu / c.eff;
+        if (best < 0 || better(cost, waves, best_cost, best_waves)) {
+            best = i;
+            best_cost = cost;
+            best_waves = waves;
+        }
+    }
+    return best;
+}
+
+int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_t stream, int forced_cus,
+           int* describe_out) {
+    int st = DG_OK;
+    const DeviceInfo* dev = nullptr;
+    int units = forced_cus;
+    if (units <= 0) {
+        dev = device_info(&st);
+        if (!dev) return st;
+        units = effective_cus(dev->cus);
+    }
+    int count = 0;
+    const KernelConfig* cfgs = dg::kernel_configs(&count);
+    const int ci = choose_config(layout, m_for_plan, p.n, units, dev, max_m_hint);
+    if (ci < 0) return DG_ERR_UNSUPPORTED;
+    const KernelConfig& c = cfgs[ci];
+    const int per_cu = dev ? dev->occ[ci] : 1;
+
+    p.tiles_n = (int)ceil_div(p.n, c.bn);
+    if (layout == dg::kMasked) {
+        p.tiles_m = (int)ceil_div(p.rows, c.bm);
+        p.num_tiles = p.num_groups * p.tiles_m * p.tiles_n;
+    } else {
+        p.tiles_m = (int)ceil_div(p.rows, c.bm);
+        p.num_tiles = p.tiles_m * p.tiles_n;
+    }
+    p.group_m = 4;
+    long slots = (long)units * per_cu;
+    long grid = p.num_tiles < slots ? p.num_tiles : slots;
+    if (grid < 1) grid = 1;
+    // keep whole rounds of 8 workgroups so the XCD hand-out stays a bijection
+    p.xcd_remap = (grid % kXcds == 0) ? 1 : 0;
+
+    if (describe_out) {
+        describe_out[0] = c.bm;
+        describe_out[1] = c.bn;
+        describe_out[2] = c.wm * c.wn;
+        describe_out[3] = p.num_tiles;
+        describe_out[4] = (int)grid;
+        describe_out[5] = c.id;
+        return DG_OK;
+    }
+    if (debug_enabled())
+        std::fprintf(stderr, "[dg] layout=%d rows=%d n=%d k=%d groups=%d cfg=%d (%dx%d, %d waves) tiles=%d grid=%ld units=%d\n",
+                     layout, p.rows, p.n, p.k, p.num_groups, c.id, c.bm, c.bn, c.wm * c.wn, p.num_tiles, grid, units);
+    if (c.launch(p, (int)grid, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
+    }
+    return DG_OK;
+}
+
+int check_common(int n, int k, const void* b, const float* sb, const void* d) {
+    if (n < 0 || k < 0) return DG_ERR_INVALID_ARG;
+    if (k == 0 || k % kKBlock != 0) return DG_ERR_UNSUPPORTED;
+    if (n % 16 != 0) return DG_ERR_UNSUPPORTED;
+    if (n > 0 && (!b || !sb || !d)) return DG_ERR_INVALID_ARG;
+    if ((b && !aligned16(b)) || (sb && !aligned16(sb)) || (d && !aligned16(d))) return DG_ERR_MISALIGNED;
+    return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dg_status_string(int status) {
+    switch (status) {
+        case DG_OK: return "DG_OK";
+        case DG_ERR_INVALID_ARG: return "DG_ERR_INVALID_ARG";
+        case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED";
+        case DG_ERR_MISALIGNED: return "DG_ERR_MISALIGNED";
+        case DG_ERR_HIP: return "DG_ERR_HIP";
+        default: return "DG_ERR_UNKNOWN";
+    }
+}
+
+int dg_get_m_alignment(void) { return kMAlign; }
+
+int dg_set_num_cus(int n) {
+    if (n < 0) return DG_ERR_INVALID_ARG;
+    g_cu_cap.store(n);
+    return DG_OK;
+}
+
+int dg_get_num_cus(void) {
+    int st = DG_OK;
+    const DeviceInfo* dev = device_info(&st);
+    if (!dev) {
+        const int cap = g_cu_cap.load();
+        return cap > 0 ? cap : st;
+    }
+    return effective_cus(dev->cus);
+}
+
+int dg_set_kernel_config(int config_id) {
+    if (config_id == -1) {
+        for (auto& f : g_forced_cfg) f.store(-1);
+        return DG_OK;
+    }
+    int count = 0;
+    const KernelConfig* cfgs = dg::kernel_configs(&count);
+    for (int i = 0; i < count; ++i) {
+        if (cfgs[i].id == config_id) {
+            g_forced_cfg[cfgs[i].layout].store(i);
+            return DG_OK;
+        }
+    }
+    return DG_ERR_INVALID_ARG;
+}
+
+int dg_kernel_config_info(int index, int* out) {
+    int count = 0;
+    const KernelConfig* cfgs = dg::kernel_configs(&count);
+    if (!out || index < 0 || index >= count) return DG_ERR_INVALID_ARG;
+    out[0] = cfgs[index].id;
+    out[1] = cfgs[index].layout;
+    out[2] = cfgs[index].bm;
+    out[3] = cfgs[index].bn;
+    out[4] = cfgs[index].wm * cfgs[index].wn;
+    return DG_OK;
+}
+
+int dg_plan_tiles(int m, int n, int num_units, int blocks_per_unit, const int* block_ms, int n_bm,
+                  const int* block_ns, int n_bn, const double* eff, int* out) {
+    if (m <= 0 || n <= 0 || num_units <= 0 || blocks_per_unit <= 0 || !block_ms || !block_ns || n_bm <= 0 ||
+        n_bn <= 0 || !out)
+        return DG_ERR_INVALID_ARG;
+    int best = -1;
+    double best_cost = 0.0;
+    long best_waves = 0;
+    for (int i = 0; i < n_bm; ++i) {
+        for (int j = 0; j < n_bn; ++j) {
+            const int bm = block_ms[i], bn = block_ns[j];
+            if (bm <= 0 || bn <= 0) return DG_ERR_INVALID_ARG;
+            const double e = eff ? eff[i * n_bn + j] : 1.0;
+            if (!(e > 0.0)) continue;
+            const long tiles = ceil_div(m, bm) * ceil_div(n, bn);
+            const long waves = ceil_div(tiles, (long)num_units * blocks_per_unit);
+            const double cost = (double)waves * bm * bn / e;
+            if (best < 0 || better(cost, waves, best_cost, best_waves)) {
+                best = i * n_bn + j;
+                best_cost = cost;
+                best_waves = waves;
+                out[0] = bm;
+                out[1] = bn;
+                out[2] = (int)tiles;
+                out[3] = (int)waves;
+            }
+        }
+    }
+    return best < 0 ? DG_ERR_INVALID_ARG : best;
+}
+
+int dg_describe_launch(int layout, int m, int n, int k, int num_groups, int num_cus, int* out) {
+    if (!out || m < 0 || n <= 0 || k <= 0 || num_groups < 1 || layout < 0 || layout > 2) return DG_ERR_INVALID_ARG;
+    GemmParams p{};
+    p.rows = m;
+    p.n = n;
+    p.k = k;
+    p.kblocks = k / kKBlock;
+    p.nblocks = (int)ceil_div(n, kKBlock);
+    p.num_groups = layout == dg::kDense ? 1 : num_groups;
+    const int units = num_cus > 0 ? effective_cus(num_cus) : 0;
+    return launch(layout, p, m, m, nullptr, units, out);
+}
+
+int dg_gemm_fp8_nt(const void* a, long lda, const float* sa, long ld_sa, const void* b, long ldb, const float* sb,
+                   void* d, long ldd, int m, int n, int k, void* stream) {
+    int st = check_common(n, k, b, sb, d);
+    if (st != DG_OK) return st;
+    if (m < 0) return DG_ERR_INVALID_ARG;
+    if (m == 0 || n == 0) return DG_OK;
+    if (!a || !sa) return DG_ERR_INVALID_ARG;
+    if (lda < k || ldb < k || ldd < n || ld_sa < m) return DG_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(sa) || lda % 16 || ldb % 16 || ldd % 8 || ld_sa % 4) return DG_ERR_MISALIGNED;
+    if ((long)m * lda > LONG_MAX / 2) return DG_ERR_UNSUPPORTED;
+    GemmParams p{};
+    p.a = static_cast<const uint8_t*>(a);
+    p.lda = lda;
+    p.sa = sa;
+    p.ld_sa = ld_sa;
+    p.b = static_cast<const uint8_t*>(b);
+    p.ldb = ldb;
+    p.sb = sb;
+    p.d = static_cast<uint16_t*>(d);
+    p.ldd = ldd;
+    p.rows = m;
+    p.n = n;
+    p.k = k;
+    p.kblocks = k / kKBlock;
+    p.nblocks = (int)ceil_div(n, kKBlock);
+    p.num_groups = 1;
+    return launch(dg::kDense, p, m, m, static_cast<hipStream_t>(stream), 0, nullptr);
+}
+
+int dg_m_grouped_gemm_fp8_contiguous(const void* a, const float* sa, long ld_sa, const void* b, const float* sb,
+                                     void* d, const int* m_indices, int m_total, int n, int k, int num_groups,
+                                     void* stream) {
+    int st = check_common(n, k, b, sb, d);
+    if (st != DG_OK) return st;
+    if (m_total < 0 || num_groups < 1) return DG_ERR_INVALID_ARG;
+    if (m_total % kMAlign != 0) return DG_ERR_INVALID_ARG;
+    if (m_total == 0 || n == 0) return DG_OK;
+    if (!a || !sa || !m_indices) return DG_ERR_INVALID_ARG;
+    if (ld_sa < m_total) return DG_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(sa) || k % 16 || ld_sa % 4 || (reinterpret_cast<uintptr_t>(m_indices) & 3u))
+        return DG_ERR_MISALIGNED;
+    GemmParams p{};
+    p.a = static_cast<const uint8_t*>(a);
+    p.lda = k;
+    p.sa = sa;
+    p.ld_sa = ld_sa;
+    p.b = static_cast<const uint8_t*>(b);
+    p.ldb = k;
+    p.b_gstride = (long)n * k;
+    p.sb = sb;
+    p.sb_gstride = ceil_div(n, kKBlock) * (k / kKBlock);
+    p.d = static_cast<uint16_t*>(d);
+    p.ldd = n;
+    p.m_indices = m_indices;
+    p.rows = m_total;
+    p.n = n;
+    p.k = k;
+    p.kblocks = k / kKBlock;
+    p.nblocks = (int)ceil_div(n, kKBlock);
+    p.num_groups = num_groups;
+    return launch(dg::kContiguous, p, m_total, m_total, static_cast<hipStream_t>(stream), 0, nullptr);
+}
+
+int dg_m_grouped_gemm_fp8_masked(const void* a, const float* sa, long ld_sa, const void* b, const float* sb,
+                                 void* d, const int* masked_m, int num_groups, int max_m, int n, int k,
+                                 void* stream) {
+    int st = check_common(n, k, b, sb, d);
+    if (st != DG_OK) return st;
+    if (max_m < 0 || num_groups < 1) return DG_ERR_INVALID_ARG;
+    if (num_groups > kMaxMaskedGroups) return DG_ERR_UNSUPPORTED;
+    if (max_m == 0 || n == 0) return DG_OK;
+    if (!a || !sa || !masked_m) return DG_ERR_INVALID_ARG;
+    if (ld_sa < max_m) return DG_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(sa) || k % 16 || ld_sa % 4 || (reinterpret_cast<uintptr_t>(masked_m) & 3u))
+        return DG_ERR_MISALIGNED;
+    GemmParams p{};
+    p.a = static_cast<const uint8_t*>(a);
+    p.lda = k;
+    p.a_gstride = (long)max_m * k;
+    p.sa = sa;
+    p.ld_sa = ld_sa;
+    p.sa_gstride = (long)(k / kKBlock) * ld_sa;
+    p.b = static_cast<const uint8_t*>(b);
+    p.ldb = k;
+    p.b_gstride = (long)n * k;
+    p.sb = sb;
+    p.sb_gstride = ceil_div(n, kKBlock) * (k / kKBlock);
+    p.d = static_cast<uint16_t*>(d);
+    p.ldd = n;
+    p.d_gstride = (long)max_m * n;
+    p.masked_m = masked_m;
+    p.rows = max_m;
+    p.n = n;
+    p.k = k;
+    p.kblocks = k / kKBlock;
+    p.nblocks = (int)ceil_div(n, kKBlock);
+    p.num_groups = num_groups;
+    return launch(dg::kMasked, p, max_m, max_m, static_cast<hipStream_t>(stream), 0, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) fine-grained-scaled FP8 E4M3 "NT" GEMM
+ * library (libdg.so).
+ *
+ * The operation (all three layouts reduce to it), from "DeepGEMM: clean and
+ * efficient FP8 GEMM kernels with fine-grained scaling" (nipponese.news
+ * translation of the project README), intro and usage paragraphs:
+ *
+ *     D[m, n] = bf16( sum_kb  sA[m, kb] * sB[n / 128, kb] * sum_{k in kb} A[m, k] * B[n, k] )
+ *
+ *   A  : E4M3 (OCP E4M3FN bytes), [M, K] row-major, K contiguous ("non-transposed LHS")
+ *   B  : E4M3, [N, K] row-major, K contiguous ("transposed RHS"); only NT is supported
+ *   sA : fp32, one scale per (row, 128-wide K block), stored MN-major (the README's
+ *        "LHS scaling factors must be transposed"): sa[kb * ld_sa + m]
+ *   sB : fp32, one scale per (128-row N block, 128-wide K block): sb[nb * (K/128) + kb]
+ *   D  : BF16 bits, [M, N] row-major, round-to-nearest-even from the fp32 accumulator
+ *
+ * Each K block's partial product is multiplied by sA*sB and added into an fp32
+ * accumulator, K blocks in ascending order (the README's two-level "promotion";
+ * the per-1x128 / per-128x128 granularity is DeepSeek-V3's fine-grained scheme).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named a, sa, b, sb, d, m_indices, masked_m are DEVICE pointers owned by
+ *    the caller.  The library never allocates, frees, synchronises or reads device
+ *    memory on the host, so every call is asynchronous on `stream` and may be
+ *    captured into a hipGraph.  `stream` is a hipStream_t (NULL = default stream).
+ *  - The return value reports host-side validation and launch errors only
+ *    (DG_OK on success).  Nothing is launched when validation fails.
+ *  - Requirements checked on the host: non-null pointers for non-empty problems;
+ *    K > 0 and K % 128 == 0 (else DG_ERR_UNSUPPORTED); N % 16 == 0 (else
+ *    DG_ERR_UNSUPPORTED); a, b, d, sa, sb 16-byte aligned; lda, ldb multiples of 16
+ *    and >= K; ldd a multiple of 8 and >= N; ld_sa a multiple of 4 and >= the row
+ *    count (else DG_ERR_MISALIGNED / DG_ERR_INVALID_ARG).
+ *  - M == 0 (or all masked_m == 0) is a valid no-op.
+ *  - Calls on distinct streams may run concurrently; the only library state is the
+ *    CU cap (dg_set_num_cus) and a per-device property cache.
+ */
+#ifndef DG_H
+#define DG_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    DG_OK = 0,
+    DG_ERR_INVALID_ARG = -1,   /* null pointer, negative size, leading dimension too small */
+    DG_ERR_UNSUPPORTED = -2,   /* shape outside what the kernels handle (K % 128, N % 16) */
+    DG_ERR_MISALIGNED = -3,    /* pointer or leading dimension alignment */
+    DG_ERR_HIP = -4            /* a HIP runtime call or the kernel launch failed */
+};
+
+/* Human-readable name of a status code.  Never NULL; the string is static. */
+const char* dg_status_string(int status);
+
+/* Row alignment that every expert segment of the contiguous layout must be padded
+ * to (the README's contiguous-layout paragraph: segments aligned to the GEMM
+ * M-block size).  Always 128. */
+int dg_get_m_alignment(void);
+
+/* Cap on the number of compute units the GEMM kernels spread over (the README's
+ * utility functions set_num_sms / get_num_sms).  n == 0 removes the cap; n < 0 is
+ * DG_ERR_INVALID_ARG.  Returns DG_OK.  Process-wide. */
+int dg_set_num_cus(int n);
+
+/* The CU count the kernels will use on the current device: the cap if one is set
+ * and smaller, else the device's CU count.  Returns a negative status if no HIP
+ * device is usable and no cap is set. */
+int dg_get_num_cus(void);
+
+/* Dense NT GEMM (the README's basic non-grouped gemm_fp8_fp8_bf16_nt).
+ *   a  [m][lda]          E4M3, K-major           b  [n][ldb]        E4M3, K-major
+ *   sa [k/128][ld_sa]    fp32, MN-major          sb [ceil(n/128)][k/128] fp32
+ *   d  [m][ldd]          BF16 bits (uint16)
+ * All rows 0..m-1 and columns 0..n-1 of d are written; nothing else is. */
+int dg_gemm_fp8_nt(const void* a, long lda,
+                   const float* sa, long ld_sa,
+                   const void* b, long ldb,
+                   const float* sb,
+                   void* d, long ldd,
+                   int m, int n, int k, void* stream);
+
+/* M-grouped GEMM, contiguous layout (the README's contiguous-layout paragraph:
+ * experts share N and K; their token segments are concatenated along M and each
+ * segment is padded to dg_get_m_alignment() rows).
+ *   a  [m_total][k]  E4M3          sa [k/128][ld_sa] fp32 MN-major (ld_sa >= m_total)
+ *   b  [G][n][k]     E4M3          sb [G][ceil(n/128)][k/128] fp32
+ *   d  [m_total][n]  BF16 bits
+ *   m_indices [m_total] int32: the group of each row, or -1 for a padding row.
+ * Device-side precondition (not checked on the host): within each aligned 128-row
+ * block every non-negative entry is the same group and the block's first row is
+ * not padding unless the whole block is.  Rows with -1 are not written.
+ * m_total must be a multiple of 128 (DG_ERR_INVALID_ARG otherwise). */
+int dg_m_grouped_gemm_fp8_contiguous(const void* a, const float* sa, long ld_sa,
+                                     const void* b, const float* sb,
+                                     void* d, const int* m_indices,
+                                     int m_total, int n, int k, int num_groups,
+                                     void* stream);
+
+/* M-grouped GEMM, masked layout (the README's masked-layout paragraph: for decode
+ * under graph capture, where the host does not know how many rows each expert
+ * received; only the valid rows are computed).
+ *   a  [G][max_m][k]  E4M3         sa [G][k/128][ld_sa] fp32 MN-major (ld_sa >= max_m)
+ *   b  [G][n][k]      E4M3         sb [G][ceil(n/128)][k/128] fp32
+ *   d  [G][max_m][n]  BF16 bits
+ *   masked_m [G] int32 (device): valid rows of each group, clamped to [0, max_m]
+ *   on the device.  Rows >= masked_m[g] of d are never written (bit-exact). */
+int dg_m_grouped_gemm_fp8_masked(const void* a, const float* sa, long ld_sa,
+                                 const void* b, const float* sb,
+                                 void* d, const int* masked_m,
+                                 int num_groups, int max_m, int n, int k,
+                                 void* stream);
+
+/* Pin the kernel configuration (an id reported by dg_describe_launch) for every
+ * later call of that configuration's layout, overriding the planner; -1 restores
+ * automatic planning for all layouts.  Meant for tuning and for tests that
+ * compare tile shapes.  Unknown ids give DG_ERR_INVALID_ARG.  Process-wide. */
+int dg_set_kernel_config(int config_id);
+
+/* Enumerate the compiled kernel configurations: for index 0, 1, ... fills
+ * out[0..4] = config id, layout, block_m, block_n, waves per workgroup and returns
+ * DG_OK; past the last one returns DG_ERR_INVALID_ARG.  Host only. */
+int dg_kernel_config_info(int index, int* out);
+
+/* Host-only tile planner, exposed for inspection and tests; it touches no device.
+ * Among candidate block shapes (block_ms[i], block_ns[j]) with per-shape relative
+ * throughput eff[i * n_bn + j] (NULL = all 1), pick the one that minimises
+ *     ceil(tiles / slots) * block_m * block_n / eff,
+ * tiles = ceil(m / block_m) * ceil(n / block_n), slots = num_units * blocks_per_unit.
+ * This is the unaligned-block-size rule of the README's optimisation section
+ * (M=256, N=7168 on 132 SMs: 128x128 fills 112 SMs, 128x112 fills 128).
+ * Ties go to fewer waves, then to the earlier candidate.  out[0..3] = block_m, block_n, tiles, waves.
+ * Returns the index i * n_bn + j of the chosen pair, or DG_ERR_INVALID_ARG. */
+int dg_plan_tiles(int m, int n, int num_units, int blocks_per_unit,
+                  const int* block_ms, int n_bm, const int* block_ns, int n_bn,
+                  const double* eff, int* out);
+
+/* Describe the kernel configuration a call with these sizes would launch, without
+ * launching (layout 0 dense, 1 contiguous, 2 masked).  out[0..5] = block_m,
+ * block_n, waves per workgroup, tiles (upper bound for masked), persistent grid
+ * size, config id.  num_cus <= 0 uses dg_get_num_cus().  Needs no device if
+ * num_cus > 0 and assumes one resident workgroup per CU for the big shapes. */
+int dg_describe_launch(int layout, int m, int n, int k, int num_groups, int num_cus, int* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

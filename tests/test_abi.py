@@ -1,0 +1,126 @@
+"""Host-side checks of libdg.so that need no GPU: it loads, exports every symbol
+the public header declares, validates arguments before touching a device, and its
+tile planner reproduces the pages' unaligned-block-size example."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_block_scaled_e4m3_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dg.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+        assert hasattr(dg, name), f"python binding lacks {name}"
+
+
+def test_status_strings(lib):
+    assert dg.status_string(0) == "DG_OK"
+    for code, name in [(-1, "DG_ERR_INVALID_ARG"), (-2, "DG_ERR_UNSUPPORTED"), (-3, "DG_ERR_MISALIGNED"),
+                       (-4, "DG_ERR_HIP")]:
+        assert dg.status_string(code) == name
+    assert dg.status_string(12345) == "DG_ERR_UNKNOWN"
+
+
+def test_m_alignment_and_cu_cap(lib):
+    assert dg.dg_get_m_alignment() == 128
+    assert lib.dg_set_num_cus(-1) == dg.DG_ERR_INVALID_ARG
+    assert lib.dg_set_num_cus(100) == 0
+    assert lib.dg_get_num_cus() == 100            # no device here: the cap is reported
+    assert lib.dg_set_num_cus(0) == 0
+
+
+def test_kernel_configs_listed(lib):
+    cfgs = dg.dg_kernel_config_info()
+    layouts = {c["layout"] for c in cfgs}
+    assert layouts == {0, 1, 2}
+    for c in cfgs:
+        assert c["block_m"] % 16 == 0 and c["block_n"] % 16 == 0
+        if c["layout"] == 1:
+            assert 128 % c["block_m"] == 0        # a tile never spans two segments
+    assert lib.dg_set_kernel_config(999) == dg.DG_ERR_INVALID_ARG
+    assert lib.dg_set_kernel_config(-1) == 0
+
+
+def _call_dense(lib, a=16, sa=16, b=16, sb=16, d=16, lda=512, ld_sa=128, ldb=512, ldd=128, m=128, n=128, k=512):
+    P = ctypes.c_void_p
+    return lib.dg_gemm_fp8_nt(P(a), lda, P(sa), ld_sa, P(b), ldb, P(sb), P(d), ldd, m, n, k, None)
+
+
+def test_dense_validation_before_any_device_work(lib):
+    assert _call_dense(lib, k=500) == dg.DG_ERR_UNSUPPORTED
+    assert _call_dense(lib, k=0) == dg.DG_ERR_UNSUPPORTED
+    assert _call_dense(lib, n=120, ldd=128) == dg.DG_ERR_UNSUPPORTED
+    assert _call_dense(lib, m=-1) == dg.DG_ERR_INVALID_ARG
+    assert _call_dense(lib, a=0) == dg.DG_ERR_INVALID_ARG
+    assert _call_dense(lib, b=0) == dg.DG_ERR_INVALID_ARG
+    assert _call_dense(lib, a=24) == dg.DG_ERR_MISALIGNED
+    assert _call_dense(lib, lda=520) == dg.DG_ERR_MISALIGNED
+    assert _call_dense(lib, ldd=130) == dg.DG_ERR_MISALIGNED
+    assert _call_dense(lib, ld_sa=64) == dg.DG_ERR_INVALID_ARG
+    assert _call_dense(lib, lda=256) == dg.DG_ERR_INVALID_ARG
+    assert _call_dense(lib, m=0) == dg.DG_OK           # empty problem: no-op, no device needed
+
+
+def test_grouped_validation(lib):
+    P = ctypes.c_void_p
+    c = lib.dg_m_grouped_gemm_fp8_contiguous
+    assert c(P(16), P(16), 256, P(16), P(16), P(16), P(16), 200, 128, 256, 2, None) == dg.DG_ERR_INVALID_ARG
+    assert c(P(16), P(16), 256, P(16), P(16), P(16), P(16), 256, 128, 256, 0, None) == dg.DG_ERR_INVALID_ARG
+    assert c(P(16), P(16), 256, P(16), P(16), P(16), None, 256, 128, 256, 2, None) == dg.DG_ERR_INVALID_ARG
+    assert c(P(16), P(16), 256, P(16), P(16), P(16), P(16), 0, 128, 256, 2, None) == dg.DG_OK
+    mk = lib.dg_m_grouped_gemm_fp8_masked
+    assert mk(P(16), P(16), 256, P(16), P(16), P(16), P(16), 2, 256, 128, 100, None) == dg.DG_ERR_UNSUPPORTED
+    assert mk(P(16), P(16), 256, P(16), P(16), P(16), P(16), 2000, 256, 128, 256, None) == dg.DG_ERR_UNSUPPORTED
+    assert mk(P(16), P(16), 100, P(16), P(16), P(16), P(16), 2, 256, 128, 256, None) == dg.DG_ERR_INVALID_ARG
+    assert mk(P(16), P(16), 256, P(16), P(16), P(16), P(16), 2, 0, 128, 256, None) == dg.DG_OK
+
+
+def test_plan_reproduces_unaligned_block_example(lib):
+    """The pages' worked example: M=256, N=7168, BLOCK_M=128 on 132 units -- 128x128 tiles
+    fill 112 units, 128x112 tiles fill 128, and the planner prefers the latter."""
+    rows = []
+    for line in open(os.path.join(GOLDEN, "unaligned_block_fill.txt")):
+        if line.strip() and not line.startswith("#"):
+            rows.append([int(x) for x in line.split()])
+    for m, n, units, bm, bn, tiles in rows:
+        _, pbm, pbn, ptiles, waves = dg.dg_plan_tiles(m, n, units, [bm], [bn])
+        assert (pbm, pbn, ptiles, waves) == (bm, bn, tiles, 1)
+    m, n, units = rows[0][:3]
+    _, bm, bn, tiles, waves = dg.dg_plan_tiles(m, n, units, [128], list(range(16, 257, 16)))
+    assert (bm, bn, tiles, waves) == (128, 112, 128, 1)
+
+
+def test_plan_fills_256_cus():
+    _, bm, bn, tiles, waves = dg.dg_plan_tiles(256, 7168, 256, [64, 128], list(range(16, 257, 16)))
+    assert (bm, bn, tiles, waves) == (64, 112, 256, 1)
+
+
+def test_describe_launch_shapes():
+    d = dg.dg_describe_launch(0, 4096, 7168, 7168, 1, 256)
+    assert (d["block_m"], d["block_n"], d["tiles"]) == (256, 224, 512) and d["grid"] == 256
+    d = dg.dg_describe_launch(0, 256, 7168, 2048, 1, 256)
+    assert (d["block_m"], d["block_n"], d["tiles"]) == (64, 112, 256)
+    d = dg.dg_describe_launch(1, 33280, 4096, 7168, 8, 256)
+    assert d["block_m"] == 128 and d["tiles"] == 260 * 4096 // d["block_n"]
+    d = dg.dg_describe_launch(2, 256, 4096, 7168, 16, 256)
+    assert d["block_m"] == 256 and d["tiles"] == 16 * 4096 // d["block_n"]

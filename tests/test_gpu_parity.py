@@ -1,0 +1,294 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Small and ragged shapes are compared element by element over the whole output;
+the full-size workloads are run in the launch configuration the bench times and
+checked on sampled rows (all columns) against the oracle, plus whole-output
+properties: no NaN/Inf, untouched padding / masked rows bit-exact, grouped output
+equal to the dense kernel's output per group bit for bit.
+"""
+import numpy as np
+import pytest
+
+import fp8_block_scaled_e4m3_amd as dg
+import workloads as W
+from tests.gpu_support import (bits, check_values, require_gpu, sample_rows, say, sentinel_like, to_dev,
+                               upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    dev = require_gpu()
+    dg.load_library()
+    yield dev
+    dg.dg_set_kernel_config(-1)
+    dg.dg_set_num_cus(0)
+
+
+def configs_of(layout):
+    return [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == layout]
+
+
+def run_dense(dd, cfg=-1, pad_cols=16):
+    """GPU dense GEMM into a sentinel-filled buffer wider than N; returns (out bits, full bits)."""
+    import torch
+    dv = upload(dd)
+    m, n = dd["a"].shape[0], dd["b"].shape[0]
+    full = sentinel_like((m, n + pad_cols))
+    dg.dg_set_kernel_config(cfg)
+    dg.dg_gemm_fp8_nt(dv["a"], dv["sa"], dv["b"], dv["sb"], full[:, :n])
+    torch.cuda.synchronize()
+    dg.dg_set_kernel_config(-1)
+    fb = bits(full)
+    return fb[:, :n], fb
+
+
+def oracle_dense(orc, dd, rows=None):
+    a, sa = dd["a"], dd["sa"]
+    if rows is not None:
+        a, sa = a[rows], sa[:, rows]
+    return orc.gemm_fp8_nt(a, sa, dd["b"], dd["sb"])
+
+
+# --------------------------------------------------------------------------- dense
+def test_dense_small_workload_all_configs(orc):
+    dd = W.make(W.WORKLOADS["dense_m128_n128_k512"])
+    ref = oracle_dense(orc, dd)
+    outs = []
+    for cfg in [-1] + configs_of(0):
+        say(f"dense 128x128x512 cfg={cfg}")
+        out, full = run_dense(dd, cfg)
+        check_values(out, ref, f"dense128 cfg{cfg}")
+        assert np.all(full[:, 128:] == W.SENTINEL_BF16)
+        outs.append(out)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])          # identical arithmetic in every tile shape
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (17, 48, 256), (300, 208, 384), (129, 400, 640),
+                                   (513, 1040, 1024), (64, 7168 // 4, 128)])
+def test_dense_ragged_shapes(orc, m, n, k):
+    dd = W.make_dense(m, n, k, seed=m + n + k)
+    ref = oracle_dense(orc, dd)
+    outs = []
+    for cfg in configs_of(0):
+        say(f"dense ragged m={m} n={n} k={k} cfg={cfg}")
+        out, full = run_dense(dd, cfg)
+        check_values(out, ref, f"dense {m}x{n}x{k} cfg{cfg}")
+        assert np.all(full[:, n:] == W.SENTINEL_BF16), "wrote past column n"
+        outs.append(out)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_dense_under_filled_workload_full_compare(orc):
+    dd = W.make(W.WORKLOADS["dense_m256_n7168_k2048"])
+    say("dense 256x7168x2048 (planned config)", dg.dg_describe_launch(0, 256, 7168, 2048, 1))
+    out, _ = run_dense(dd)
+    ref = oracle_dense(orc, dd)
+    check_values(out, ref, "dense 256x7168x2048")
+
+
+def test_dense_prefill_workload_sampled(orc):
+    dd = W.make(W.WORKLOADS["dense_m4096_n7168_k7168"])
+    say("dense 4096x7168x7168 (planned config)", dg.dg_describe_launch(0, 4096, 7168, 7168, 1))
+    out, full = run_dense(dd)
+    assert np.all(full[:, 7168:] == W.SENTINEL_BF16)
+    assert not np.any(out == W.SENTINEL_BF16)
+    rows = sample_rows(4096, 256, 48)
+    ref = oracle_dense(orc, dd, rows)
+    check_values(out[rows], ref, "dense 4096x7168x7168 sampled rows")
+
+
+def test_dense_cu_cap_is_bit_identical(orc):
+    dd = W.make_dense(512, 1024, 512, seed=77)
+    base, _ = run_dense(dd)
+    for cap in (37, 64):
+        dg.dg_set_num_cus(cap)
+        say(f"dense 512x1024x512 with cu cap {cap}")
+        out, _ = run_dense(dd)
+        dg.dg_set_num_cus(0)
+        assert np.array_equal(out, base)
+    check_values(base, oracle_dense(orc, dd), "dense 512x1024x512")
+
+
+# --------------------------------------------------------------------------- contiguous
+def run_contiguous(cd, cfg=-1):
+    import torch
+    dv = upload(cd)
+    out = sentinel_like((cd["m_total"], cd["n"]))
+    dg.dg_set_kernel_config(cfg)
+    dg.dg_m_grouped_gemm_fp8_contiguous(dv["a"], dv["sa"], dv["b"], dv["sb"], out, dv["m_indices"])
+    torch.cuda.synchronize()
+    dg.dg_set_kernel_config(-1)
+    return bits(out)
+
+
+def dense_gpu_segment(cd, g, lo, hi):
+    """The dense kernel on one group's rows (its own call) for bit-exact comparison."""
+    seg = {"a": cd["a"][lo:hi], "sa": np.ascontiguousarray(cd["sa"][:, lo:hi]), "b": cd["b"][g],
+           "sb": cd["sb"][g]}
+    seg["sa"] = np.pad(seg["sa"], ((0, 0), (0, (-seg["sa"].shape[1]) % 4)))
+    out, _ = run_dense(seg)
+    return out
+
+
+def test_contiguous_small_all_configs(orc):
+    counts = [130, 0, 1, 257, 128]
+    cd = W.make_contiguous(counts, n=272, k=384, seed=21)
+    sentinel = np.full((cd["m_total"], 272), W.SENTINEL_BF16, np.uint16)
+    ref = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], cd["m_indices"], d_init=sentinel)
+    valid = cd["m_indices"] >= 0
+    outs = []
+    for cfg in configs_of(1):
+        say(f"contiguous small counts={counts} cfg={cfg}")
+        out = run_contiguous(cd, cfg)
+        check_values(out[valid], ref[valid], f"contiguous small cfg{cfg}")
+        assert np.all(out[~valid] == W.SENTINEL_BF16), "a padding row was written"
+        outs.append(out)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    off = 0
+    for g, (c, p) in enumerate(zip(counts, W.padded(counts))):
+        if c:
+            assert np.array_equal(dense_gpu_segment(cd, g, off, off + c), outs[0][off:off + c])
+        off += p
+
+
+def test_contiguous_workload_sampled(orc):
+    w = W.WORKLOADS["contiguous_g8_t32768_zipf1.1_n4096_k7168"]
+    cd = W.make(w)
+    say("contiguous 8x4096x7168 zipf (planned config)",
+        dg.dg_describe_launch(1, cd["m_total"], 4096, 7168, 8))
+    out = run_contiguous(cd)
+    valid = cd["m_indices"] >= 0
+    assert np.all(out[~valid] == W.SENTINEL_BF16)
+    assert not np.any(out[valid] == W.SENTINEL_BF16)
+    off = 0
+    rows, groups = [], []
+    for g, (c, p) in enumerate(zip(cd["counts"], W.padded(cd["counts"]))):
+        r = off + sample_rows(c, 128, 6, seed=g)
+        rows.extend(r.tolist())
+        groups.extend([g] * len(r))
+        off += p
+    rows = np.array(rows)
+    ref = np.empty((len(rows), 4096), np.uint16)
+    for g in range(8):
+        sel = np.array(groups) == g
+        ref[sel] = orc.gemm_fp8_nt(cd["a"][rows[sel]], cd["sa"][:, rows[sel]], cd["b"][g], cd["sb"][g])
+    check_values(out[rows], ref, "contiguous workload sampled rows")
+    # grouped == dense per group, bit for bit, on the smallest group
+    lo = sum(W.padded(cd["counts"])[:7])
+    assert np.array_equal(dense_gpu_segment(cd, 7, lo, lo + cd["counts"][7]), out[lo:lo + cd["counts"][7]])
+
+
+# --------------------------------------------------------------------------- masked
+def run_masked(md, cfg=-1, masked_m=None):
+    import torch
+    dv = upload(md)
+    if masked_m is not None:
+        dv["masked_m"] = to_dev(np.asarray(masked_m, np.int32))
+    out = sentinel_like((md["groups"], md["max_m"], md["n"]))
+    dg.dg_set_kernel_config(cfg)
+    dg.dg_m_grouped_gemm_fp8_masked(dv["a"], dv["sa"], dv["b"], dv["sb"], out, dv["masked_m"])
+    torch.cuda.synchronize()
+    dg.dg_set_kernel_config(-1)
+    return bits(out)
+
+
+def check_masked(orc, md, out, groups=None):
+    mm = np.clip(md["masked_m"], 0, md["max_m"])
+    for g in range(md["groups"]):
+        assert np.all(out[g, mm[g]:] == W.SENTINEL_BF16), f"group {g}: a row >= masked_m was written"
+        assert not np.any(out[g, :mm[g]] == W.SENTINEL_BF16), f"group {g}: a valid row was not written"
+    for g in (range(md["groups"]) if groups is None else groups):
+        if mm[g] == 0:
+            continue
+        rows = np.arange(mm[g]) if mm[g] <= 64 else sample_rows(int(mm[g]), 16, 24, seed=g)
+        ref = orc.gemm_fp8_nt(md["a"][g][rows], md["sa"][g][:, rows], md["b"][g], md["sb"][g])
+        check_values(out[g][rows], ref, f"masked group {g}")
+
+
+@pytest.mark.parametrize("max_m", [256, 70])
+def test_masked_edges_all_configs(orc, max_m):
+    mm = [0, max_m, 1, max_m - 1, 16, 17, min(128, max_m), min(129, max_m), 0, 33]
+    md = W.make_masked(len(mm), max_m, 272, 256, seed=31, masked_m=mm)
+    outs = []
+    for cfg in configs_of(2):
+        say(f"masked edges max_m={max_m} cfg={cfg}")
+        out = run_masked(md, cfg)
+        check_masked(orc, md, out)
+        outs.append(out)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    for g in (1, 3, 5):
+        seg = {"a": md["a"][g][:mm[g]], "sa": md["sa"][g][:, :mm[g]], "b": md["b"][g], "sb": md["sb"][g]}
+        seg["sa"] = np.pad(seg["sa"], ((0, 0), (0, (-mm[g]) % 4)))
+        dense, _ = run_dense(seg)
+        assert np.array_equal(dense, outs[0][g, :mm[g]])
+
+
+def test_masked_out_of_range_counts_are_clamped(orc):
+    md = W.make_masked(3, 64, 128, 128, seed=32, masked_m=[-3, 500, 5])
+    out = run_masked(md)
+    assert np.all(out[0] == W.SENTINEL_BF16)
+    md2 = dict(md, masked_m=np.array([0, 64, 5], np.int32))
+    check_masked(orc, md2, out)
+
+
+def test_masked_all_empty_is_noop():
+    md = W.make_masked(4, 256, 128, 128, seed=33, masked_m=[0, 0, 0, 0])
+    out = run_masked(md)
+    assert np.all(out == W.SENTINEL_BF16)
+
+
+def test_masked_workload_sampled(orc):
+    md = W.make(W.WORKLOADS["masked_g16_cap256_n4096_k7168"])
+    say("masked 16x256x4096x7168 masked_m=", md["masked_m"].tolist(),
+        dg.dg_describe_launch(2, 256, 4096, 7168, 16))
+    out = run_masked(md)
+    check_masked(orc, md, out)
+
+
+def test_masked_graph_replay_reads_device_counts(orc):
+    """The masked call captured once in a graph follows masked_m changed on the device
+    between replays (the host never reads it)."""
+    import torch
+    md = W.make_masked(6, 128, 256, 256, seed=34, masked_m=[5, 0, 128, 64, 1, 100])
+    dv = upload(md)
+    out = sentinel_like((6, 128, 256))
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):      # warm-up outside capture
+        dg.dg_m_grouped_gemm_fp8_masked(dv["a"], dv["sa"], dv["b"], dv["sb"], out, dv["masked_m"])
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dg.dg_m_grouped_gemm_fp8_masked(dv["a"], dv["sa"], dv["b"], dv["sb"], out, dv["masked_m"])
+    for counts in ([5, 0, 128, 64, 1, 100], [128, 3, 0, 17, 128, 0], [1, 1, 1, 1, 1, 1]):
+        say(f"graph replay masked_m={counts}")
+        out.fill_(W.SENTINEL_BF16)
+        dv["masked_m"].copy_(torch.tensor(counts, dtype=torch.int32))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = bits(out)
+        eager = run_masked(md, masked_m=counts)
+        assert np.array_equal(got, eager)
+        check_masked(orc, dict(md, masked_m=np.array(counts, np.int32)), got)
+
+
+# --------------------------------------------------------------------------- errors
+def test_binding_reports_validation_errors():
+    import torch
+    a = torch.zeros((64, 200), dtype=torch.uint8, device="cuda:0")
+    b = torch.zeros((64, 200), dtype=torch.uint8, device="cuda:0")
+    sa = torch.ones((2, 64), device="cuda:0")
+    sb = torch.ones((1, 2), device="cuda:0")
+    d = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_gemm_fp8_nt(a, sa, b, sb, d)
+    assert e.value.status == dg.DG_ERR_UNSUPPORTED
+    assert torch.count_nonzero(d).item() == 0
