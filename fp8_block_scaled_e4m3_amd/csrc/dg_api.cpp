@@ -116,12 +116,11 @@ int choose_config(int layout, int m, int n, int num_units, const DeviceInfo* dev
             if (c.bm != want) continue;
             return i;
         }
-        const int per_cu = dev ? dev->occ[i] : 1;
+        // The busiest CU's share: ceil(tiles / CUs) tiles of bm x bn at the shape's
+        // relative throughput (workgroups resident together share one CU).
         const long tiles = ceil_div(m, c.bm) * ceil_div(n, c.bn);
-        const long slots = (long)num_units * per_cu;
-        const long waves = ceil_div(tiles, slots);
-        // per-CU work of one wave of tiles; several resident blocks share one CU
-        const double cost = (double)waves * c.bm * c.bn * per_cu / c.eff;
+        const long waves = ceil_div(tiles, (long)num_units);
+        const double cost = (double)waves * c.bm * c.bn / c.eff;
         if (best < 0 || better(cost, waves, best_cost, best_waves)) {
             best = i;
             best_cost = cost;

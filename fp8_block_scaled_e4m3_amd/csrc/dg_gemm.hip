@@ -42,6 +42,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
 
 constexpr int kKBlock = 128;        // K bytes per scale block == K of one MFMA
 constexpr int kMaxMaskedGroups = 1024;
@@ -52,33 +54,51 @@ constexpr int kXcds = 8;
 // 8 and 16 consecutive rows read at one logical chunk hit distinct bank groups.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
+// Raw buffer descriptor over `bytes` bytes from `base` (clamped to 4 GiB - 1).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+    const unsigned n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFl ? 0xFFFFFFFFu : (unsigned)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
+}
+
+// One fp32 from a buffer (per-lane byte offset + scalar byte offset).
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+// A value every lane holds identically, moved to a scalar register.
+__device__ __forceinline__ float uniform(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
 __device__ __forceinline__ void wait_vmem_all() {
     // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maximum.
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Copy 8 consecutive 128-byte rows into LDS (one wave instruction, 1 KB).
-// `row_ptr` is this lane's source row; chunk = lane % 8 ^ swz(row).
-__device__ __forceinline__ void dma_rows8(const uint8_t* row_ptr, int lrow8, int lane,
-                                          uint8_t* lds_dst) {
-    const int pc = lane & 7;
-    const int lc = pc ^ swz(lrow8);
-    __builtin_amdgcn_global_load_lds((const void*)(row_ptr + lc * 16), (lds_void*)lds_dst, 16, 0, 0);
-}
-
-template <int BM, int BN, int WM, int WN, int LAYOUT>
+// MF selects the matrix instruction: 16 -> V_MFMA_F32_16X16X128_F8F6F4 (one
+// instruction per 128-K block of a 16x16 sub-tile), 32 -> V_MFMA_F32_32X32X64_F8F6F4
+// (two instructions per 128-K block of a 32x32 sub-tile; the second accumulates
+// onto the first, so the promoted quantity is still the whole block's partial).
+// The 32x32 form needs one scale product per 16 promotion FMAs instead of per 4,
+// and its 32-column sub-tiles never straddle a 128-column scale block when the
+// tile offsets are multiples of 32.
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF>
 __global__ void __launch_bounds__(WM * WN * 64)
-dg_gemm_kernel(const GemmParams p) {
+dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const float* __restrict__ sa_ptr,
+               const uint8_t* __restrict__ b_ptr, const float* __restrict__ sb_ptr, uint16_t* __restrict__ d_ptr) {
     constexpr int NW = WM * WN;
-    constexpr int NT = NW * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int FM = WTM / MF, FN = WTN / MF;
+    constexpr int NACC = MF * MF / 64;             // accumulator floats per lane per sub-tile
     constexpr int ROWS = BM + BN;
     constexpr int STAGE = ROWS * kKBlock;
-    constexpr int LOADS = ROWS / 8;
-    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
+    constexpr int A_SLOTS = BM / 8, B_SLOTS = BN / 8;
+    constexpr int A_PER = (A_SLOTS + NW - 1) / NW, B_PER = (B_SLOTS + NW - 1) / NW;
+    static_assert(MF == 16 || MF == 32, "matrix instruction shape");
+    static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "block rows must be a multiple of 8");
-    static_assert(WTN <= 128, "a wave's columns may touch at most two B scale blocks");
+    static_assert(WTN <= 256, "a wave's columns touch at most three B scale blocks");
+    typedef float vacc __attribute__((ext_vector_type(NACC)));
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
@@ -88,7 +108,8 @@ dg_gemm_kernel(const GemmParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
-    const int lrow = lane & 15, lgrp = lane >> 4;
+    const int lsub = lane & (MF - 1);             // row of the sub-tile this lane feeds / owns
+    const int lgrp = lane / MF;                   // K group of the lane inside an operand fragment
     const int KB = p.kblocks;
 
     // ---- masked layout: valid row blocks per group, exclusive prefix in LDS ----
@@ -168,126 +189,238 @@ dg_gemm_kernel(const GemmParams p) {
         valid_rows = valid_rows > BM ? BM : valid_rows;
         const int m0 = mb * BM, n0 = nb * BN;
 
-        const uint8_t* a_base = p.a + (LAYOUT == kMasked ? (long)g * p.a_gstride : 0);
-        const float* sa_base = p.sa + (LAYOUT == kMasked ? (long)g * p.sa_gstride : 0);
-        const uint8_t* b_base = p.b + (long)g * p.b_gstride;
-        const float* sb_base = p.sb + (long)g * p.sb_gstride;
-        uint16_t* d_base = p.d + (LAYOUT == kMasked ? (long)g * p.d_gstride : 0);
-        const int a_last = p.rows - 1, b_last = p.n - 1;
+        const int a_last = p.rows - 1 - m0;   // last readable row, relative to the tile
+        const int b_last = p.n - 1 - n0;
+        const uint8_t* a_tile = a_ptr + (LAYOUT == kMasked ? (long)g * p.a_gstride : 0) + (long)m0 * p.lda;
+        const uint8_t* b_tile = b_ptr + (long)g * p.b_gstride + (long)n0 * p.ldb;
+        const float* sa_tile = sa_ptr + (LAYOUT == kMasked ? (long)g * p.sa_gstride : 0) + m0;
+        const float* sb_grp = sb_ptr + (long)g * p.sb_gstride;
+        uint16_t* d_base = d_ptr + (LAYOUT == kMasked ? (long)g * p.d_gstride : 0);
 
-        // ---- this lane's rows for the operand copies (clamped: tails read real rows) ----
-        auto issue_stage = [&](uint8_t* smem, int kb) {
-            for (int j = wave; j < LOADS; j += NW) {
-                const int srow = j * 8 + (lane >> 3);
-                const uint8_t* src;
-                if (j * 8 < BM) {
-                    int r = m0 + srow;
-                    r = r > a_last ? a_last : r;
-                    src = a_base + (long)r * p.lda + (long)kb * kKBlock;
-                } else {
-                    int r = n0 + srow - BM;
-                    r = r > b_last ? b_last : r;
-                    src = b_base + (long)r * p.ldb + (long)kb * kKBlock;
-                }
-                dma_rows8(src, srow, lane, smem + j * 1024);
+        // ---- operand copies: 8-row slots dealt round robin to the waves; each lane's
+        // 32-bit source offset inside the tile is fixed for the whole K loop (tails
+        // are clamped to the last real row) ----
+        uint32_t a_off[A_PER], b_off[B_PER];
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            const int srow = min(wave + i * NW, A_SLOTS - 1) * 8 + (lane >> 3);
+            const int r = srow > a_last ? a_last : srow;
+            a_off[i] = (uint32_t)r * (uint32_t)p.lda + (uint32_t)((((lane & 7) ^ swz(srow))) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) {
+            const int srow = min(wave + i * NW, B_SLOTS - 1) * 8 + (lane >> 3);
+            const int r = srow > b_last ? b_last : srow;
+            b_off[i] = (uint32_t)r * (uint32_t)p.ldb + (uint32_t)((((lane & 7) ^ swz(BM + srow))) * 16);
+        }
+        // Buffer descriptors over this tile's operands: the K offset of each stage
+        // travels in a scalar register, so issuing a stage costs no vector ALU work.
+        const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a_tile, (long)(a_last + 1) * p.lda);
+        const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b_tile, (long)(b_last + 1) * p.ldb);
+        // DMA slot t of this wave (A slots first, then B slots) for K block kb.  A slot
+        // index past the last one repeats the last slot: the same bytes land on the
+        // same LDS location twice, which keeps the issue free of branches.
+        constexpr int NSLOT = A_PER + B_PER;
+        auto issue_slot = [&](uint8_t* smem, int kb, int t) {
+            const int koff = kb * kKBlock;
+            if (t < A_PER) {
+                const int j = min(wave + t * NW, A_SLOTS - 1);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void*)(smem + j * 1024), 16,
+                                                         (int)a_off[t], koff, 0, 0);
+            } else {
+                const int j = min(wave + (t - A_PER) * NW, B_SLOTS - 1);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(smem + BM * kKBlock + j * 1024), 16,
+                                                         (int)b_off[t - A_PER], koff, 0, 0);
             }
+        };
+        auto issue_stage = [&](uint8_t* smem, int kb) {
+#pragma unroll
+            for (int t = 0; t < NSLOT; ++t) issue_slot(smem, kb, t);
         };
 
         // ---- per-lane scale sources ----
-        const float* sa_lane[FM];
+        uint32_t sa_off[FM];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            int r = m0 + wm * WTM + fm * 16 + lrow;
-            r = r > a_last ? a_last : r;
-            sa_lane[fm] = sa_base + r;
+            const int r = wm * WTM + fm * MF + lsub;
+            sa_off[fm] = (uint32_t)(r > a_last ? a_last : r) * 4u;
         }
+        // Sub-tile column fn (MF columns, inside one 128-column scale block because MF
+        // divides 128 and the column offsets are multiples of MF) reads its B scales
+        // from row nb(fn) of sB; the byte offset of that row is wave-uniform.
+        // With MF=16 a wave spans at most 128 columns, i.e. two scale rows (lo, hi):
+        // two loads per K block and a per-column choice by a uniform bit mask.
         const int wcol0 = n0 + wn * WTN;
-        const int nb_lo = min(wcol0 / kKBlock, p.nblocks - 1);
-        const int nb_hi = min(nb_lo + 1, p.nblocks - 1);
-        unsigned hi_mask = 0;   // bit fn set: sub-tile fn uses nb_hi
+        constexpr int NSB = MF == 16 ? 2 : FN;
+        int sb_off[NSB];
+        unsigned hi_mask = 0;
+        if constexpr (MF == 16) {
+            const int nb_lo = min(wcol0 / kKBlock, p.nblocks - 1);
+            sb_off[0] = nb_lo * KB * 4;
+            sb_off[1] = min(nb_lo + 1, p.nblocks - 1) * KB * 4;
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            if ((wcol0 + fn * 16) / kKBlock > nb_lo) hi_mask |= 1u << fn;
-        const float* sb_lo_ptr = sb_base + (long)nb_lo * KB;
-        const float* sb_hi_ptr = sb_base + (long)nb_hi * KB;
+            for (int fn = 0; fn < FN; ++fn)
+                if ((wcol0 + fn * MF) / kKBlock > nb_lo) hi_mask |= 1u << fn;
+        } else {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                sb_off[fn] = min((wcol0 + fn * MF) / kKBlock, p.nblocks - 1) * KB * 4;
+        }
+        const __amdgpu_buffer_rsrc_t rs_sa = make_rsrc(sa_tile, ((long)KB * p.ld_sa - m0) * 4);
+        const __amdgpu_buffer_rsrc_t rs_sb = make_rsrc(sb_grp, (long)p.nblocks * KB * 4);
         const bool wave_active = wm * WTM < valid_rows;
 
-        v4f acc[FM][FN];
+        vacc acc[FM][FN];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = vacc{};
 
-        // per-lane LDS byte offsets of the two 16-byte halves of a fragment row
-        const int c0 = ((2 * lgrp) ^ swz(lrow)) * 16;
-        const int c1 = ((2 * lgrp + 1) ^ swz(lrow)) * 16;
-
-        struct Scales { float a[FM]; float bl, bh; };
-        auto load_scales = [&](Scales& sc, int kb) {
+        // per-lane LDS byte offsets of the 16-byte chunks of this lane's fragment
+        // (MF=16: chunks 2g, 2g+1 of the 128-K row; MF=32: chunks 4h+2g, 4h+2g+1 for
+        // K half h), swizzled like the rows were written
+        int coff[2][2];
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) sc.a[fm] = sa_lane[fm][(long)kb * p.ld_sa];
-            sc.bl = sb_lo_ptr[kb];
-            sc.bh = sb_hi_ptr[kb];
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                coff[h][e] = (((MF == 16 ? 2 * lgrp : 4 * h + 2 * lgrp) + e) ^ swz(lane & 15)) * 16;
+
+        struct Scales { float a[FM]; float b[NSB]; };
+        auto load_scales = [&](Scales& sc, int kb) {
+            const int soff = kb * p.ld_sa * 4;
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) sc.a[fm] = load_f32(rs_sa, (int)sa_off[fm], soff);
+#pragma unroll
+            for (int t = 0; t < NSB; ++t) sc.b[t] = load_f32(rs_sb, 0, sb_off[t] + kb * 4);
         };
 
-        auto compute_stage = [&](const uint8_t* smem, const Scales& sc) {
-            if (!wave_active) return;
-            v8i af[FM];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const uint8_t* rowp = smem + (wm * WTM + fm * 16 + lrow) * kKBlock;
-                const v4i lo = *(const v4i*)(rowp + c0);
-                const v4i hi = *(const v4i*)(rowp + c1);
-                af[fm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        // One K block on this wave's sub-tiles, as a flat sequence over (fn, fm).
+        // The promotion of the partial issued kLag steps earlier follows each step's
+        // MFMA(s), so the VALU consumes results that finished long ago while the
+        // matrix core works on the next ones.
+        // The copies of the next stage (K block nkb into nsmem, whose previous contents
+        // every wave finished with before the barrier that precedes this call) are
+        // issued one at a time between this stage's MFMAs, so the address FIFO of the
+        // texture unit never backs up behind a burst of them.
+        // Past the last K block the copy re-reads block KB-1 into the idle buffer.
+        auto compute_stage = [&](const uint8_t* smem, const Scales& sc, uint8_t* nsmem, int nkb, Scales& sc_next) {
+            nkb = nkb < KB ? nkb : KB - 1;
+            if (!wave_active) {
+                issue_stage(nsmem, nkb);
+                load_scales(sc_next, nkb);
+                return;
             }
+            constexpr int NJ = FN * FM;
+            constexpr int kLag = MF == 32 ? 1 : (NJ >= 32 ? 2 : 3);
+            // This lane's byte offsets for the call, made opaque to the compiler so that
+            // every fragment read is stage + offset + an immediate row offset instead
+            // of a separately hoisted address register per fragment and stage.  Only
+            // the offset is hidden: the stage array stays visible, so the compiler
+            // knows these reads never touch the buffer the copies are filling.
+            lds_u8* lbase[2][2];
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const uint8_t* rowp = smem + (BM + wn * WTN + fn * 16 + lrow) * kKBlock;
-                const v4i lo = *(const v4i*)(rowp + c0);
-                const v4i hi = *(const v4i*)(rowp + c1);
-                const v8i bf = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                const float sbv = ((hi_mask >> fn) & 1u) ? sc.bh : sc.bl;
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf, af[fm], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                    const float s = sc.a[fm] * sbv;
-                    acc[fm][fn][0] = __builtin_fmaf(part[0], s, acc[fm][fn][0]);
-                    acc[fm][fn][1] = __builtin_fmaf(part[1], s, acc[fm][fn][1]);
-                    acc[fm][fn][2] = __builtin_fmaf(part[2], s, acc[fm][fn][2]);
-                    acc[fm][fn][3] = __builtin_fmaf(part[3], s, acc[fm][fn][3]);
+                for (int e = 0; e < 2; ++e) {
+                    int off = lsub * kKBlock + coff[h][e];
+                    asm volatile("" : "+v"(off));
+                    lbase[h][e] = (lds_u8*)smem + off;
                 }
+            // fragment of sub-tile rows [row0, row0+MF) for K half h (MF=16: whole block)
+            auto frag = [&](int row0, int h) -> v8i {
+                const v4i lo = *(const lds_v4i*)(lbase[h][0] + row0 * kKBlock);
+                const v4i hi = *(const lds_v4i*)(lbase[h][1] + row0 * kKBlock);
+                return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            };
+            constexpr int NH = MF == 32 ? 2 : 1;
+            v8i af[FM][NH];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int h = 0; h < NH; ++h) af[fm][h] = frag(wm * WTM + fm * MF, h);
+            v8i bf[NH], bnext[1];
+#pragma unroll
+            for (int h = 0; h < NH; ++h) bf[h] = frag(BM + wn * WTN, h);
+            bnext[0] = bf[0];
+            vacc part[kLag + 1];
+            // scale of sub-tile column fn for fragment row fm
+            float sbl = 0.f, sbh = 0.f;
+            if constexpr (MF == 16) {
+                sbl = uniform(sc.b[0]);
+                sbh = uniform(sc.b[NSB - 1]);
             }
+            auto scale = [&](int fm, int fn) {
+                if constexpr (MF == 16) return sc.a[fm] * (((hi_mask >> fn) & 1u) ? sbh : sbl);
+                else return sc.a[fm] * sc.b[fn];
+            };
+            auto promote = [&](int j, int i0, int i1, float s) {
+                const int fn = j / FM, fm = j % FM;
+                const vacc& pj = part[j % (kLag + 1)];
+#pragma unroll
+                for (int i = i0; i < i1; ++i) acc[fm][fn][i] = __builtin_fmaf(pj[i], s, acc[fm][fn][i]);
+            };
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int fn = j / FM, fm = j % FM;
+                if constexpr (MF == 16) {
+                    if (fm == 0 && fn + 1 < FN) bnext[0] = frag(BM + wn * WTN + (fn + 1) * MF, 0);
+                    part[j % (kLag + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bf[0], af[fm][0], vacc{}, 0, 0, 0, 0, 0, 0);
+                    if (j >= kLag) promote(j - kLag, 0, NACC, scale((j - kLag) % FM, (j - kLag) / FM));
+                    if (fm == FM - 1) bf[0] = bnext[0];
+                } else {
+                    // each K half's B fragment is reloaded for the next sub-tile column as
+                    // soon as the MFMA that reads it has been issued
+                    const bool reload = fm == FM - 1 && fn + 1 < FN;
+                    float s = 0.f;
+                    part[j % (kLag + 1)] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bf[0], af[fm][0], vacc{}, 0, 0, 0, 0, 0, 0);
+                    if (reload) bf[0] = frag(BM + wn * WTN + (fn + 1) * MF, 0);
+                    if (j >= kLag) {
+                        s = scale((j - kLag) % FM, (j - kLag) / FM);
+                        promote(j - kLag, 0, NACC / 2, s);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    part[j % (kLag + 1)] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bf[1], af[fm][1], part[j % (kLag + 1)], 0, 0, 0, 0, 0, 0);
+                    if (reload) bf[1] = frag(BM + wn * WTN + (fn + 1) * MF, 1);
+                    if (j >= kLag) promote(j - kLag, NACC / 2, NACC, s);
+                }
+#pragma unroll
+                for (int t = 0; t < NSLOT; ++t)
+                    if (j == t * NJ / NSLOT) issue_slot(nsmem, nkb, t);
+                if (j == NJ / 2) load_scales(sc_next, nkb);
+                // keep this order: the scheduler would otherwise pull each promotion up
+                // against its own MFMA and stall on the result
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int j = NJ - kLag; j < NJ; ++j) promote(j, 0, NACC, scale(j % FM, j / FM));
         };
 
         // ---- K loop: two LDS stages, loop unrolled by two so stage buffers are static.
-        // The scales of K block kb+1 are fetched while block kb is consumed. ----
+        // Block kb+1's copies and scales are issued while block kb is consumed. ----
         Scales sc0, sc1;
         load_scales(sc0, 0);
         issue_stage(smem0, 0);
         for (int kb = 0; kb < KB; kb += 2) {
             wait_vmem_all();
             __syncthreads();
-            if (kb + 1 < KB) {
-                issue_stage(smem1, kb + 1);
-                load_scales(sc1, kb + 1);
-            }
-            compute_stage(smem0, sc0);
+            compute_stage(smem0, sc0, smem1, kb + 1, sc1);
             if (kb + 1 >= KB) break;
             wait_vmem_all();
             __syncthreads();
-            if (kb + 2 < KB) {
-                issue_stage(smem0, kb + 2);
-                load_scales(sc0, kb + 2);
-            }
-            compute_stage(smem1, sc1);
+            compute_stage(smem1, sc1, smem0, kb + 2, sc0);
         }
 
-        // ---- epilogue: BF16 RNE, 8-byte stores, skip padding / masked / tail rows ----
+        // ---- epilogue: BF16 RNE, 8-byte stores, skip padding / masked / tail rows.
+        // A lane owns row lsub of each sub-tile and runs of four adjacent columns:
+        // MF=16: columns 4g..4g+3; MF=32: columns 8q+4g..8q+4g+3, q = 0..3. ----
         if (wave_active) {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                const int lr = wm * WTM + fm * 16 + lrow;     // row inside the tile
+                const int lr = wm * WTM + fm * MF + lsub;     // row inside the tile
                 bool row_ok = lr < valid_rows;
                 if constexpr (LAYOUT == kContiguous) {
                     if (row_ok) row_ok = p.m_indices[m0 + lr] >= 0;
@@ -296,14 +429,17 @@ dg_gemm_kernel(const GemmParams p) {
                 uint16_t* drow = d_base + (long)(m0 + lr) * p.ldd;
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
-                    const int col = wcol0 + fn * 16 + lgrp * 4;
-                    if (col < p.n) {
-                        v4bf o;
-                        o.x = (__bf16)acc[fm][fn][0];
-                        o.y = (__bf16)acc[fm][fn][1];
-                        o.z = (__bf16)acc[fm][fn][2];
-                        o.w = (__bf16)acc[fm][fn][3];
-                        *(v4bf*)(drow + col) = o;
+#pragma unroll
+                    for (int q = 0; q < NACC / 4; ++q) {
+                        const int col = wcol0 + fn * MF + q * 8 + lgrp * 4;
+                        if (col < p.n) {
+                            v4bf o;
+                            o.x = (__bf16)acc[fm][fn][4 * q + 0];
+                            o.y = (__bf16)acc[fm][fn][4 * q + 1];
+                            o.z = (__bf16)acc[fm][fn][4 * q + 2];
+                            o.w = (__bf16)acc[fm][fn][4 * q + 3];
+                            *(v4bf*)(drow + col) = o;
+                        }
                     }
                 }
             }
@@ -312,33 +448,37 @@ dg_gemm_kernel(const GemmParams p) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF>
 static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT>), dim3(grid), dim3(WM * WN * 64), 0, s, p);
+    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF>), dim3(grid), dim3(WM * WN * 64), 0, s, p, p.a,
+                       p.sa, p.b, p.sb, p.d);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF>
 static hipError_t occupancy_cfg(int* blocks) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks, reinterpret_cast<const void*>(&dg_gemm_kernel<BM, BN, WM, WN, LAYOUT>), WM * WN * 64, 0);
+        blocks, reinterpret_cast<const void*>(&dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF>), WM * WN * 64, 0);
 }
 
-#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, EFF) \
-    {ID, LAYOUT, BM, BN, WM, WN, EFF, &launch_cfg<BM, BN, WM, WN, LAYOUT>, &occupancy_cfg<BM, BN, WM, WN, LAYOUT>}
+#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, EFF)                                      \
+    {ID, LAYOUT, BM, BN, WM, WN, EFF, &launch_cfg<BM, BN, WM, WN, LAYOUT, MF>,            \
+     &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF>}
 
 static const KernelConfig kConfigs[] = {
     // dense
-    DG_CFG(0, kDense, 256, 224, 4, 2, 1.00),
-    DG_CFG(1, kDense, 256, 256, 4, 2, 1.00),
-    DG_CFG(2, kDense, 128, 128, 2, 2, 0.55),
-    DG_CFG(3, kDense, 64, 112, 4, 1, 0.35),
+    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 1.00),
+    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 0.90),
+    DG_CFG(2, kDense, 128, 128, 4, 1, 32, 0.55),
+    DG_CFG(3, kDense, 64, 112, 4, 1, 16, 0.35),
     // contiguous (BLOCK_M = the 128-row segment alignment)
-    DG_CFG(10, kContiguous, 128, 256, 2, 4, 1.00),
-    DG_CFG(11, kContiguous, 128, 128, 2, 2, 0.55),
+    DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 1.00),
+    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 0.55),
+    DG_CFG(12, kContiguous, 128, 256, 4, 2, 32, 0.95),
     // masked
-    DG_CFG(20, kMasked, 256, 128, 4, 2, 1.00),
-    DG_CFG(21, kMasked, 128, 128, 2, 2, 1.00),
+    DG_CFG(20, kMasked, 256, 128, 4, 2, 16, 1.00),
+    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 1.00),
+    DG_CFG(22, kMasked, 256, 128, 8, 1, 32, 0.95),
 };
 
 const KernelConfig* kernel_configs(int* count) {
