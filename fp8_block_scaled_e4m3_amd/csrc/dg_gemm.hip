@@ -70,9 +70,23 @@ __device__ __forceinline__ float uniform(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
-__device__ __forceinline__ void wait_vmem_all() {
-    // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maximum.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+// Workgroup barrier without a memory fence.  __syncthreads() also fences, which
+// drains every outstanding load of the wave, including the copies of younger
+// stages that should stay in flight; the callers wait for exactly what they need
+// (wait_vmem_le) first.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maximum: at most N of
+// this wave's vector memory loads may still be outstanding (they complete in order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // MF selects the matrix instruction: 16 -> V_MFMA_F32_16X16X128_F8F6F4 (one
@@ -82,7 +96,7 @@ __device__ __forceinline__ void wait_vmem_all() {
 // The 32x32 form needs one scale product per 16 promotion FMAs instead of per 4,
 // and its 32-column sub-tiles never straddle a 128-column scale block when the
 // tile offsets are multiples of 32.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST>
 __global__ void __launch_bounds__(WM * WN * 64)
 dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const float* __restrict__ sa_ptr,
                const uint8_t* __restrict__ b_ptr, const float* __restrict__ sb_ptr, uint16_t* __restrict__ d_ptr) {
@@ -100,8 +114,13 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     static_assert(WTN <= 256, "a wave's columns touch at most three B scale blocks");
     typedef float vacc __attribute__((ext_vector_type(NACC)));
 
+    // NST stage buffers, each its own array so the compiler can prove that fragment
+    // reads of one stage never alias the copies in flight into another.
+    static_assert(NST >= 2 && NST <= 4, "2..4 LDS stages");
     __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem2[NST > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem3[NST > 3 ? STAGE : 16];
     __shared__ int s_prefix[LAYOUT == kMasked ? kMaxMaskedGroups + 1 : 1];
 
     const int tid = threadIdx.x;
@@ -399,19 +418,28 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             for (int j = NJ - kLag; j < NJ; ++j) promote(j, 0, NACC, scale(j % FM, j / FM));
         };
 
-        // ---- K loop: two LDS stages, loop unrolled by two so stage buffers are static.
-        // Block kb+1's copies and scales are issued while block kb is consumed. ----
-        Scales sc0, sc1;
-        load_scales(sc0, 0);
-        issue_stage(smem0, 0);
-        for (int kb = 0; kb < KB; kb += 2) {
-            wait_vmem_all();
-            __syncthreads();
-            compute_stage(smem0, sc0, smem1, kb + 1, sc1);
-            if (kb + 1 >= KB) break;
-            wait_vmem_all();
-            __syncthreads();
-            compute_stage(smem1, sc1, smem0, kb + 2, sc0);
+        // ---- K loop over NST LDS stages, unrolled by NST so every buffer is a named
+        // array.  Stage kb+NST-1's copies and scales are issued while block kb is
+        // consumed; before consuming block kb a wave waits only for its own loads of
+        // that block, leaving the younger stages' loads in flight. ----
+        constexpr int NVM = NSLOT + FM + NSB;      // vector memory instructions per stage
+        Scales sc[NST];
+        uint8_t* const stage_buf[4] = {smem0, smem1, smem2, smem3};
+#pragma unroll
+        for (int s = 0; s < NST - 1; ++s) {
+            const int kk = s < KB ? s : KB - 1;
+            load_scales(sc[s], kk);
+            issue_stage(stage_buf[s], kk);
+        }
+        for (int kb = 0; kb < KB; kb += NST) {
+#pragma unroll
+            for (int u = 0; u < NST; ++u) {
+                if (kb + u >= KB) break;
+                wait_vmem_le<(NST - 2) * NVM>();
+                stage_barrier();
+                compute_stage(stage_buf[u], sc[u], stage_buf[(u + NST - 1) % NST], kb + u + NST - 1,
+                              sc[(u + NST - 1) % NST]);
+            }
         }
 
         // ---- epilogue: BF16 RNE, 8-byte stores, skip padding / masked / tail rows.
@@ -444,41 +472,45 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 }
             }
         }
-        __syncthreads();   // every wave is done with both stages before the next tile
+        // the redundant copies issued past the last K block must land before the next
+        // tile (or another workgroup) reuses these buffers; then every wave is done
+        wait_vmem_le<0>();
+        __syncthreads();
     }
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST>
 static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF>), dim3(grid), dim3(WM * WN * 64), 0, s, p, p.a,
+    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST>), dim3(grid), dim3(WM * WN * 64), 0, s, p, p.a,
                        p.sa, p.b, p.sb, p.d);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST>
 static hipError_t occupancy_cfg(int* blocks) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks, reinterpret_cast<const void*>(&dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF>), WM * WN * 64, 0);
+        blocks, reinterpret_cast<const void*>(&dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST>), WM * WN * 64, 0);
 }
 
-#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, EFF)                                      \
-    {ID, LAYOUT, BM, BN, WM, WN, EFF, &launch_cfg<BM, BN, WM, WN, LAYOUT, MF>,            \
-     &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF>}
+#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF)                                 \
+    {ID, LAYOUT, BM, BN, WM, WN, EFF, &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST>,       \
+     &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF, NST>}
 
 static const KernelConfig kConfigs[] = {
     // dense
-    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 1.00),
-    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 0.90),
-    DG_CFG(2, kDense, 128, 128, 4, 1, 32, 0.55),
-    DG_CFG(3, kDense, 64, 112, 4, 1, 16, 0.35),
+    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 2, 1.00),
+    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 2, 0.90),
+    DG_CFG(2, kDense, 128, 128, 2, 2, 16, 4, 0.55),
+    DG_CFG(3, kDense, 64, 112, 4, 1, 16, 4, 0.35),
+    DG_CFG(4, kDense, 128, 224, 4, 2, 16, 3, 0.80),
     // contiguous (BLOCK_M = the 128-row segment alignment)
-    DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 1.00),
-    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 0.55),
-    DG_CFG(12, kContiguous, 128, 256, 4, 2, 32, 0.95),
+    DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00),
+    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55),
+    DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95),
     // masked
-    DG_CFG(20, kMasked, 256, 128, 4, 2, 16, 1.00),
-    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 1.00),
-    DG_CFG(22, kMasked, 256, 128, 8, 1, 32, 0.95),
+    DG_CFG(20, kMasked, 256, 128, 4, 2, 16, 3, 1.00),
+    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00),
+    DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 2, 0.95),
 };
 
 const KernelConfig* kernel_configs(int* count) {
