@@ -111,10 +111,12 @@ int choose_config(int layout, int m, int n, int num_units, const DeviceInfo* dev
         const KernelConfig& c = cfgs[i];
         if (c.layout != layout) continue;
         if (layout == dg::kMasked) {
-            // the whole capacity in one row block when it fits, else the largest block
+            // the whole capacity in one row block when it fits (B is then streamed once
+            // per group), else the largest block; among those the most efficient shape
             const int want = max_m_hint <= 128 ? 128 : 256;
             if (c.bm != want) continue;
-            return i;
+            if (best < 0 || c.eff > cfgs[best].eff) best = i;
+            continue;
         }
         // The busiest CU's share: ceil(tiles / CUs) tiles of bm x bn at the shape's
         // relative throughput (workgroups resident together share one CU).

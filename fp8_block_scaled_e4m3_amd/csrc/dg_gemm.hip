@@ -179,15 +179,20 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
 
         int g = 0, mb, nb, valid_rows;
         if constexpr (LAYOUT == kMasked) {
+            // group g owns tiles [prefix[g], prefix[g+1]) * tiles_n, ordered N block
+            // major and row block minor, so the row blocks sharing one B tile are
+            // neighbours in the hand-out (same XCD, same step: B comes from L2 once)
             const int q = L / p.tiles_n;
-            nb = L % p.tiles_n;
             int lo = 0, hi = p.num_groups;           // largest g with prefix[g] <= q
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
                 if (s_prefix[mid] <= q) lo = mid; else hi = mid;
             }
             g = lo;
-            mb = q - s_prefix[g];
+            const int vb = s_prefix[g + 1] - s_prefix[g];
+            const int t = L - s_prefix[g] * p.tiles_n;
+            nb = t / vb;
+            mb = t - nb * vb;
             int mm = p.masked_m[g];
             mm = mm < 0 ? 0 : (mm > p.rows ? p.rows : mm);
             valid_rows = mm - mb * BM;
@@ -234,7 +239,10 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         }
         // Buffer descriptors over this tile's operands: the K offset of each stage
         // travels in a scalar register, so issuing a stage costs no vector ALU work.
-        const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a_tile, (long)(a_last + 1) * p.lda);
+        // Masked layout: rows at or past masked_m fall outside the descriptor, so their
+        // copies return zeros without a memory access (their outputs are never stored).
+        const int a_rows_read = LAYOUT == kMasked ? valid_rows : a_last + 1;
+        const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a_tile, (long)a_rows_read * p.lda);
         const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b_tile, (long)(b_last + 1) * p.ldb);
         // DMA slot t of this wave (A slots first, then B slots) for K block kb.  A slot
         // index past the last one repeats the last slot: the same bytes land on the
@@ -508,9 +516,10 @@ static const KernelConfig kConfigs[] = {
     DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55),
     DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95),
     // masked
-    DG_CFG(20, kMasked, 256, 128, 4, 2, 16, 3, 1.00),
+    DG_CFG(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00),
     DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00),
-    DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 2, 0.95),
+    DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90),
+    DG_CFG(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90),
 };
 
 const KernelConfig* kernel_configs(int* count) {
