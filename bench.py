@@ -32,7 +32,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("dg_gemm.hip", "dg_internal.h", "dg_api.cpp"):
+    for name in ("dg_gemm.hip", "dg_quant.hip", "dg_internal.h", "dg_api.cpp"):
         with open(os.path.join(ROOT, "fp8_block_scaled_e4m3_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -269,6 +269,29 @@ def main():
             if ww.kind == "masked":
                 sec[name]["sum_masked_m"] = int(np.clip(d2["masked_m"], 0, ww.max_m).sum())
             del d2, v2, o2, c2
+            torch.cuda.empty_cache()
+        # the FP8 cast that feeds the GEMM (fp32 in, E4M3 + scales out): HBM-bound
+        for cname, rows, k, gran in (("cast_1x128_m4096_k7168_f32", 4096, 7168, 1),
+                                     ("cast_128x128_n7168_k7168_f32", 7168, 7168, 128)):
+            say(f"bench: secondary {cname}")
+            x = torch.from_numpy(W.make_fp32_operand(rows, k, gran, seed=0)).to("cuda:0")
+            q = torch.empty((rows, k), dtype=torch.uint8, device="cuda:0")
+            if gran == 1:
+                s_ = torch.empty((k // 128, W.ld_sa_for(rows)), device="cuda:0")
+                c3 = lambda: dg.dg_quantize_fp8_1x128(x, q, s_)
+                nsc = (k // 128) * rows
+            else:
+                s_ = torch.empty((ceil_div(rows, 128), k // 128), device="cuda:0")
+                c3 = lambda: dg.dg_quantize_fp8_128x128(x, q, s_)
+                nsc = ceil_div(rows, 128) * (k // 128)
+            b3 = rows * k * 4 + rows * k + 4 * nsc
+            for _ in range(3):
+                c3()
+            mean_s, _ = time_launches(c3, args.secondary_iters, flush)
+            sec[cname] = {"us": round(mean_s * 1e6, 2), "gbps": round(b3 / mean_s / 1e9, 1),
+                          "frac_hbm": round(b3 / mean_s / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm",
+                          "caches_flushed": True, "algorithmic_bytes": b3, "traffic": traffic_for(cname)}
+            del x, q, s_, c3
             torch.cuda.empty_cache()
         result["secondary"] = sec
 

@@ -62,6 +62,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_m_grouped_gemm_fp8_contiguous.restype = I
     lib.dg_m_grouped_gemm_fp8_masked.argtypes = [P, P, L, P, P, P, P, I, I, I, I, P]
     lib.dg_m_grouped_gemm_fp8_masked.restype = I
+    lib.dg_quantize_fp8_1x128.argtypes = [P, I, L, I, I, P, L, P, L, P]
+    lib.dg_quantize_fp8_1x128.restype = I
+    lib.dg_quantize_fp8_128x128.argtypes = [P, I, L, I, I, P, L, P, P]
+    lib.dg_quantize_fp8_128x128.restype = I
     lib.dg_set_kernel_config.argtypes = [I]
     lib.dg_set_kernel_config.restype = I
     lib.dg_kernel_config_info.argtypes = [I, P]
@@ -203,6 +207,43 @@ def dg_m_grouped_gemm_fp8_masked(a, sa, b, sb, d, masked_m, stream=None) -> None
            "dg_m_grouped_gemm_fp8_masked")
 
 
+def _quant_args(x, q, name):
+    import torch
+    if x.dtype == torch.float32:
+        dt = 0
+    elif x.dtype in (torch.bfloat16,):
+        dt = 1
+    else:
+        raise TypeError(f"{name}: x must be float32 or bfloat16, got {x.dtype}")
+    px = _dev(x, "x", (torch.float32, torch.bfloat16), 2)
+    pq = _dev(q, "q", _fp8_types(), 2)
+    if tuple(q.shape) != tuple(x.shape):
+        raise ValueError(f"{name}: q shape {tuple(q.shape)} != x shape {tuple(x.shape)}")
+    return dt, px, pq
+
+
+def dg_quantize_fp8_1x128(x, q, sa, stream=None) -> None:
+    """Cast x [rows, k] (fp32/bf16) to E4M3 q with per-1x128 scales sa [k/128, ld_sa] (MN-major)."""
+    rows, k = x.shape
+    dt, px, pq = _quant_args(x, q, "dg_quantize_fp8_1x128")
+    psa = _dev(sa, "sa", _f32(), 2)
+    if sa.shape[0] != -(-k // 128) or sa.shape[1] < rows:
+        raise ValueError(f"sa shape {tuple(sa.shape)} does not fit rows={rows}, k={k}")
+    _check(load_library().dg_quantize_fp8_1x128(px, dt, x.stride(0), rows, k, pq, q.stride(0), psa, sa.stride(0),
+                                                _stream(stream)), "dg_quantize_fp8_1x128")
+
+
+def dg_quantize_fp8_128x128(x, q, sb, stream=None) -> None:
+    """Cast x [rows, k] (fp32/bf16) to E4M3 q with per-128x128 scales sb [ceil(rows/128), k/128]."""
+    rows, k = x.shape
+    dt, px, pq = _quant_args(x, q, "dg_quantize_fp8_128x128")
+    psb = _dev(sb, "sb", _f32(), 2)
+    if tuple(sb.shape) != (-(-rows // 128), -(-k // 128)) or not sb.is_contiguous():
+        raise ValueError(f"sb must be contiguous [{-(-rows // 128)}, {-(-k // 128)}], got {tuple(sb.shape)}")
+    _check(load_library().dg_quantize_fp8_128x128(px, dt, x.stride(0), rows, k, pq, q.stride(0), psb,
+                                                  _stream(stream)), "dg_quantize_fp8_128x128")
+
+
 def dg_set_kernel_config(config_id: int) -> None:
     """Pin a kernel configuration id for its layout (-1: automatic planning again)."""
     _check(load_library().dg_set_kernel_config(int(config_id)), "dg_set_kernel_config")
@@ -243,5 +284,5 @@ __all__ = [
     "DGError", "load_library", "status_string", "dg_status_string",
     "dg_get_m_alignment", "dg_set_num_cus", "dg_get_num_cus",
     "dg_gemm_fp8_nt", "dg_m_grouped_gemm_fp8_contiguous", "dg_m_grouped_gemm_fp8_masked",
-    "dg_set_kernel_config", "dg_kernel_config_info", "dg_plan_tiles", "dg_describe_launch",
+    "dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_set_kernel_config", "dg_kernel_config_info", "dg_plan_tiles", "dg_describe_launch",
 ]

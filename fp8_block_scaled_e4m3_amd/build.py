@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdg.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["dg_gemm.hip", "dg_api.cpp"]
+SOURCES = ["dg_gemm.hip", "dg_quant.hip", "dg_api.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms stay disabled; the compiler would otherwise fuse float

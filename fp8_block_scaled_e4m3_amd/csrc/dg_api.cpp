@@ -46,6 +46,18 @@ bool debug_enabled() {
     return v == 1;
 }
 
+// DG_GROUP_M (tuning): row blocks of the tile raster visited together before
+// moving along N; 0 or unset keeps the default of 4.
+int group_m_override() {
+    static int v = -1;
+    if (v < 0) {
+        const char* e = std::getenv("DG_GROUP_M");
+        v = e ? std::atoi(e) : 0;
+        if (v < 0) v = 0;
+    }
+    return v;
+}
+
 // Returns nullptr when no device is usable.
 const DeviceInfo* device_info(int* status) {
     int dev = 0;
@@ -157,7 +169,7 @@ int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_
         p.tiles_m = (int)ceil_div(p.rows, c.bm);
         p.num_tiles = p.tiles_m * p.tiles_n;
     }
-    p.group_m = 4;
+    p.group_m = group_m_override() > 0 ? group_m_override() : 4;
     long slots = (long)units * per_cu;
     long grid = p.num_tiles < slots ? p.num_tiles : slots;
     if (grid < 1) grid = 1;
@@ -239,6 +251,45 @@ int dg_set_kernel_config(int config_id) {
         }
     }
     return DG_ERR_INVALID_ARG;
+}
+
+static int check_quant(const void* x, int x_dtype, long ldx, int rows, int k, const void* q, long ldq,
+                       const float* s) {
+    if (rows < 0 || k < 0 || (x_dtype != DG_DTYPE_F32 && x_dtype != DG_DTYPE_BF16)) return DG_ERR_INVALID_ARG;
+    if (k == 0 || k % kKBlock != 0) return DG_ERR_UNSUPPORTED;
+    if (rows == 0) return DG_OK;
+    if (!x || !q || !s) return DG_ERR_INVALID_ARG;
+    if (ldx < k || ldq < k) return DG_ERR_INVALID_ARG;
+    const long esz = x_dtype == DG_DTYPE_F32 ? 4 : 2;
+    if (!aligned16(x) || (ldx * esz) % 16 || (reinterpret_cast<uintptr_t>(q) & 7u) || ldq % 8 ||
+        (reinterpret_cast<uintptr_t>(s) & 3u))
+        return DG_ERR_MISALIGNED;
+    return DG_OK;
+}
+
+int dg_quantize_fp8_1x128(const void* x, int x_dtype, long ldx, int rows, int k, void* q, long ldq, float* sa,
+                          long ld_sa, void* stream) {
+    const int st = check_quant(x, x_dtype, ldx, rows, k, q, ldq, sa);
+    if (st != DG_OK || rows == 0) return st;
+    if (ld_sa < rows) return DG_ERR_INVALID_ARG;
+    if (dg::launch_quant_1x128(x, x_dtype == DG_DTYPE_BF16, ldx, rows, k, static_cast<uint8_t*>(q), ldq, sa, ld_sa,
+                               static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
+    }
+    return DG_OK;
+}
+
+int dg_quantize_fp8_128x128(const void* x, int x_dtype, long ldx, int rows, int k, void* q, long ldq, float* sb,
+                            void* stream) {
+    const int st = check_quant(x, x_dtype, ldx, rows, k, q, ldq, sb);
+    if (st != DG_OK || rows == 0) return st;
+    if (dg::launch_quant_128x128(x, x_dtype == DG_DTYPE_BF16, ldx, rows, k, static_cast<uint8_t*>(q), ldq, sb,
+                                 static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
+    }
+    return DG_OK;
 }
 
 int dg_kernel_config_info(int index, int* out) {

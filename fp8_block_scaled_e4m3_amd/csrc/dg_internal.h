@@ -39,4 +39,10 @@ struct KernelConfig {
 // Table of compiled configurations (defined in dg_gemm.hip).
 const KernelConfig* kernel_configs(int* count);
 
+// FP8 casts with fine-grained scales (defined in dg_quant.hip).
+hipError_t launch_quant_1x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq, float* sa,
+                              long ld_sa, hipStream_t stream);
+hipError_t launch_quant_128x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq,
+                                float* sb, hipStream_t stream);
+
 }  // namespace dg

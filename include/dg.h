@@ -111,6 +111,30 @@ int dg_m_grouped_gemm_fp8_masked(const void* a, const float* sa, long ld_sa,
                                  int num_groups, int max_m, int n, int k,
                                  void* stream);
 
+/* Input element types of the casts below. */
+enum { DG_DTYPE_F32 = 0, DG_DTYPE_BF16 = 1 };
+
+/* FP8 cast with per-1x128 scales -- the "prior kernel" the README's usage paragraph
+ * asks for: it produces A and sA exactly as dg_gemm_fp8_nt and the grouped calls read
+ * them (sA MN-major, i.e. the transposed LHS scales the README requires).
+ *   x  [rows][ldx]   fp32 or bf16 (x_dtype), device       q  [rows][ldq]  E4M3 bytes
+ *   sa [k/128][ld_sa] fp32, sa[kb * ld_sa + row]
+ * Per (row, 128-K block): amax = max |x| (NaN entries ignored), scale = fp32(amax/448)
+ * (1 if amax == 0), q = E4M3 RNE of fp32(x / scale), saturating at +-448, NaN -> 0x7F.
+ * Requires k % 128 == 0 (DG_ERR_UNSUPPORTED), x 16-byte aligned with ldx a multiple of
+ * 16 bytes / element size, q 8-byte aligned with ldq % 8 == 0, ld_sa >= rows (else
+ * DG_ERR_MISALIGNED / DG_ERR_INVALID_ARG).  rows == 0 is a no-op.  Asynchronous on
+ * `stream`; nothing is allocated. */
+int dg_quantize_fp8_1x128(const void* x, int x_dtype, long ldx, int rows, int k,
+                          void* q, long ldq, float* sa, long ld_sa, void* stream);
+
+/* FP8 cast with per-128x128 scales (the B-side granularity).
+ *   x  [rows][ldx] fp32 or bf16       q [rows][ldq] E4M3       sb [ceil(rows/128)][k/128]
+ * Same rounding and requirements as dg_quantize_fp8_1x128; a ragged last row block
+ * takes its amax over the rows it has. */
+int dg_quantize_fp8_128x128(const void* x, int x_dtype, long ldx, int rows, int k,
+                            void* q, long ldq, float* sb, void* stream);
+
 /* Pin the kernel configuration (an id reported by dg_describe_launch) for every
  * later call of that configuration's layout, overriding the planner; -1 restores
  * automatic planning for all layouts.  Meant for tuning and for tests that

@@ -124,3 +124,19 @@ def test_describe_launch_shapes():
     assert d["block_m"] == 128 and d["tiles"] == 260 * 4096 // d["block_n"]
     d = dg.dg_describe_launch(2, 256, 4096, 7168, 16, 256)
     assert d["block_m"] == 256 and d["tiles"] == 16 * 4096 // d["block_n"]
+
+
+def test_quantize_validation(lib):
+    P = ctypes.c_void_p
+    q1 = lib.dg_quantize_fp8_1x128
+    assert q1(P(16), 0, 256, 4, 200, P(16), 256, P(16), 4, None) == dg.DG_ERR_UNSUPPORTED
+    assert q1(P(16), 7, 256, 4, 256, P(16), 256, P(16), 4, None) == dg.DG_ERR_INVALID_ARG
+    assert q1(P(16), 0, 256, 4, 256, P(16), 256, P(16), 2, None) == dg.DG_ERR_INVALID_ARG     # ld_sa < rows
+    assert q1(P(16), 0, 256, 4, 256, P(20), 256, P(16), 4, None) == dg.DG_ERR_MISALIGNED      # q not 8-aligned
+    assert q1(P(16), 0, 257, 4, 256, P(16), 256, P(16), 4, None) == dg.DG_ERR_MISALIGNED      # ldx*4 % 16
+    assert q1(None, 0, 256, 4, 256, P(16), 256, P(16), 4, None) == dg.DG_ERR_INVALID_ARG
+    assert q1(P(16), 0, 256, 0, 256, P(16), 256, P(16), 4, None) == dg.DG_OK                  # empty: no-op
+    q2 = lib.dg_quantize_fp8_128x128
+    assert q2(P(16), 1, 256, 4, 384, P(16), 384, P(16), None) == dg.DG_ERR_INVALID_ARG       # ldx < k
+    assert q2(P(16), 1, 388, 4, 384, P(16), 384, P(16), None) == dg.DG_ERR_MISALIGNED        # ldx*2 % 16
+    assert q2(P(16), 1, 384, 0, 384, P(16), 384, P(16), None) == dg.DG_OK

@@ -1,0 +1,154 @@
+"""GPU parity of the FP8 cast kernels (the prior-kernel cast the README leaves to the
+caller) against the oracle's quantiser: codes and scales must match bit for bit."""
+import numpy as np
+import pytest
+
+import fp8_block_scaled_e4m3_amd as dg
+import workloads as W
+from tests.gpu_support import bits, check_values, require_gpu, say, sentinel_like, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    require_gpu()
+    dg.load_library()
+
+
+def recipe(rows, k, block_rows, seed):
+    rng = np.random.default_rng(seed)
+    return W._scaled_normals(rng, rows, k, block_rows)
+
+
+def specials(x):
+    """Plant zeros, signed zeros, huge and tiny values, NaN and inf in known places."""
+    x = x.copy()
+    k = x.shape[1]
+    x[0, :128] = 0.0                          # all-zero block -> scale 1
+    x[1, :128] = -0.0
+    x[1, 5] = 0.0
+    x[2, :128] = np.float32(1e-30)            # subnormal-range codes after scaling
+    x[2, 7] = np.float32(3.0)
+    x[3, k - 2] = np.float32(1e30)            # one huge value: the rest round to 0 / tiny
+    x[4, k // 2] = np.nan                     # NaN ignored by amax, coded 0x7F
+    x[5, k - 1] = np.inf                      # amax inf: others -> +-0, inf -> NaN code
+    x[6, :128] = np.float32(448.0) * np.linspace(-1, 1, 128, dtype=np.float32)
+    x[7, :] = np.float32(2.0) ** ((np.arange(k) % 48) - 30).astype(np.float32)   # wide magnitude range
+    return x
+
+
+def as_bf16(x):
+    import torch
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    return t, t.to(torch.float32).numpy()
+
+
+def gpu_1x128(x_t, rows, k):
+    import torch
+    q = torch.empty((rows, k), dtype=torch.uint8, device="cuda:0")
+    sa = torch.full((k // 128, W.ld_sa_for(rows)), -1.0, device="cuda:0")
+    dg.dg_quantize_fp8_1x128(x_t, q, sa)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sa.cpu().numpy()
+
+
+def gpu_128x128(x_t, rows, k):
+    import torch
+    q = torch.empty((rows, k), dtype=torch.uint8, device="cuda:0")
+    sb = torch.full((-(-rows // 128), k // 128), -1.0, device="cuda:0")
+    dg.dg_quantize_fp8_128x128(x_t, q, sb)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sb.cpu().numpy()
+
+
+def same_bits(a, b):
+    return np.array_equal(np.asarray(a).view(np.uint32), np.asarray(b).view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,k", [(1, 128), (7, 384), (300, 640), (129, 1024)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_1x128_bit_exact(orc, rows, k, dtype):
+    import torch
+    x = recipe(rows, k, 1, seed=rows * 7 + k)
+    if rows >= 8:
+        x = specials(x)
+    if dtype == "bf16":
+        xt, x = as_bf16(x)
+        xt = xt.to("cuda:0")
+    else:
+        xt = to_dev(x)
+    say(f"quant 1x128 {rows}x{k} {dtype}")
+    q, sa = gpu_1x128(xt, rows, k)
+    rq, rsa = orc.quantize_rows_1x128(x)
+    assert np.array_equal(q, rq), f"{np.sum(q != rq)} codes differ"
+    assert same_bits(sa[:, :rows], rsa)
+    assert np.all(sa[:, rows:] == -1.0)                     # padding columns untouched
+
+
+@pytest.mark.parametrize("rows,k", [(128, 128), (200, 384), (1, 256), (385, 512)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_128x128_bit_exact(orc, rows, k, dtype):
+    x = recipe(rows, k, 128, seed=rows * 11 + k)
+    if rows >= 8:
+        x = specials(x)
+    if dtype == "bf16":
+        xt, x = as_bf16(x)
+        xt = xt.to("cuda:0")
+    else:
+        xt = to_dev(x)
+    say(f"quant 128x128 {rows}x{k} {dtype}")
+    q, sb = gpu_128x128(xt, rows, k)
+    rq, rsb = orc.quantize_blocks_128x128(x)
+    assert np.array_equal(q, rq), f"{np.sum(q != rq)} codes differ"
+    assert same_bits(sb, rsb)
+
+
+def test_quant_full_size_prefill_operands(orc):
+    """The prefill workload's A (4096x7168) and B (7168x7168) cast on the GPU equal the
+    oracle's cast and the shared generator's (torch-based) cast."""
+    rng = np.random.default_rng(0)
+    xa = W._scaled_normals(rng, 4096, 7168, 1)
+    say("quant 1x128 4096x7168 f32")
+    q, sa = gpu_1x128(to_dev(xa), 4096, 7168)
+    rq, rsa = orc.quantize_rows_1x128(xa)
+    assert np.array_equal(q, rq) and same_bits(sa, rsa)
+    gq, gsa = W.quant_rows_1x128(xa)
+    assert np.array_equal(q, gq) and same_bits(sa, gsa)
+    del xa
+    xb = W._scaled_normals(rng, 7168, 7168, 128)
+    say("quant 128x128 7168x7168 f32")
+    q, sb = gpu_128x128(to_dev(xb), 7168, 7168)
+    rq, rsb = orc.quantize_blocks_128x128(xb)
+    assert np.array_equal(q, rq) and same_bits(sb, rsb)
+
+
+def test_cast_then_gemm_end_to_end(orc):
+    """GPU cast of fp32 operands followed by the GPU GEMM matches the oracle GEMM of the
+    oracle's cast of the same operands."""
+    import torch
+    m, n, k = 320, 272, 640
+    rng = np.random.default_rng(5)
+    xa, xb = W._scaled_normals(rng, m, k, 1), W._scaled_normals(rng, n, k, 128)
+    qa = torch.empty((m, k), dtype=torch.uint8, device="cuda:0")
+    sa = torch.empty((k // 128, W.ld_sa_for(m)), device="cuda:0")
+    qb = torch.empty((n, k), dtype=torch.uint8, device="cuda:0")
+    sb = torch.empty((-(-n // 128), k // 128), device="cuda:0")
+    d = sentinel_like((m, n))
+    dg.dg_quantize_fp8_1x128(to_dev(xa), qa, sa)
+    dg.dg_quantize_fp8_128x128(to_dev(xb), qb, sb)
+    dg.dg_gemm_fp8_nt(qa, sa, qb, sb, d)
+    torch.cuda.synchronize()
+    ra, rsa = orc.quantize_rows_1x128(xa)
+    rb, rsb = orc.quantize_blocks_128x128(xb)
+    check_values(bits(d), orc.gemm_fp8_nt(ra, rsa, rb, rsb), "cast + gemm")
+
+
+def test_quant_validation_errors():
+    import torch
+    x = torch.zeros((4, 200), device="cuda:0")
+    q = torch.zeros((4, 200), dtype=torch.uint8, device="cuda:0")
+    sa = torch.zeros((2, 4), device="cuda:0")
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_quantize_fp8_1x128(x, q, sa)
+    assert e.value.status == dg.DG_ERR_UNSUPPORTED

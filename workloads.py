@@ -104,6 +104,11 @@ def _scaled_normals(rng, rows: int, k: int, block_rows: int) -> np.ndarray:
     return x
 
 
+def make_fp32_operand(rows: int, k: int, block_rows: int, seed: int = 0) -> np.ndarray:
+    """The recipe's fp32 values before the cast (input of the FP8 cast kernels)."""
+    return _scaled_normals(np.random.default_rng(seed), rows, k, block_rows)
+
+
 def _cast_e4m3(y: np.ndarray) -> np.ndarray:
     import torch
     t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32))
