@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dg_internal.h"
 
 namespace dg {
@@ -88,6 +90,9 @@ __device__ __forceinline__ void wait_vmem_le() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // MF selects the matrix instruction: 16 -> V_MFMA_F32_16X16X128_F8F6F4 (one
 // instruction per 128-K block of a 16x16 sub-tile), 32 -> V_MFMA_F32_32X32X64_F8F6F4
@@ -322,131 +327,232 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             for (int t = 0; t < NSB; ++t) sc.b[t] = load_f32(rs_sb, 0, sb_off[t] + kb * 4);
         };
 
-        // One K block on this wave's sub-tiles, as a flat sequence over (fn, fm).
-        // The promotion of the partial issued kLag steps earlier follows each step's
-        // MFMA(s), so the VALU consumes results that finished long ago while the
-        // matrix core works on the next ones.
-        // The copies of the next stage (K block nkb into nsmem, whose previous contents
-        // every wave finished with before the barrier that precedes this call) are
-        // issued one at a time between this stage's MFMAs, so the address FIFO of the
-        // texture unit never backs up behind a burst of them.
-        // Past the last K block the copy re-reads block KB-1 into the idle buffer.
-        auto compute_stage = [&](const uint8_t* smem, const Scales& sc, uint8_t* nsmem, int nkb, Scales& sc_next) {
-            nkb = nkb < KB ? nkb : KB - 1;
-            if (!wave_active) {
-                issue_stage(nsmem, nkb);
-                load_scales(sc_next, nkb);
-                return;
-            }
-            constexpr int NJ = FN * FM;
-            constexpr int kLag = MF == 32 ? 1 : (NJ >= 32 ? 2 : 3);
-            // This lane's byte offsets for the call, made opaque to the compiler so that
-            // every fragment read is stage + offset + an immediate row offset instead
-            // of a separately hoisted address register per fragment and stage.  Only
-            // the offset is hidden: the stage array stays visible, so the compiler
-            // knows these reads never touch the buffer the copies are filling.
-            lds_u8* lbase[2][2];
+        // ---- K loop: one continuous stream of steps over (K block, column fn, row fm).
+        // Step j of a block issues the MFMA(s) of sub-tile (fm, fn) = (j % FM, j / FM)
+        // and promotes the partial of the step kLag earlier, which may belong to the
+        // previous K block (its scales are still held), so the matrix core never
+        // waits for a promotion and a block boundary costs no pipeline drain.
+        // LDS stages: block kb lives in stage kb % NST.  In each block the single
+        // workgroup barrier follows the first MFMA of the last column (step JB).  By
+        // then every wave has finished reading this block's stage, except for the
+        // fragments already in registers, and has waited for its own copies of the
+        // next block, so after the barrier
+        //   * the next block's fragments are read while the last column's MFMAs run
+        //     (each A fragment as soon as its last MFMA of this block is issued), and
+        //   * the stage read in the previous block is free: the copies of block
+        //     kb + NST - 1 go there, issued one per step early in the next block.
+        constexpr int NJ = FN * FM;
+        constexpr int JB = (FN - 1) * FM;
+        static_assert(FN >= 2, "the barrier sits in the last of at least two columns");
+        // ring of in-flight partials: its position is a compile-time function of the
+        // step because the block loop is unrolled by NST
+        constexpr int R = MF == 32 ? 2
+                        : ((NST * NJ) % 4 == 0 ? 4 : ((NST * NJ) % 3 == 0 ? 3 : 2));
+        static_assert((NST * NJ) % R == 0, "partial ring must tile the unrolled loop");
+        constexpr int kLag = R - 1;
+        constexpr int NVM = NSLOT + FM + NSB;      // vector memory instructions per block
+        // copy slot t is issued at step jslot(t), all of them no later than step JB
+        constexpr int SP = (JB + 1) / (2 * NSLOT) > 1 ? (JB + 1) / (2 * NSLOT) : 1;
+        constexpr int JSC = kLag < JB ? kLag : JB; // scale loads of block kb + NST - 1
+
+        Scales sc[NST];
+        uint8_t* const stage_buf[4] = {smem0, smem1, smem2, smem3};
+        constexpr int NH = MF == 32 ? 2 : 1;
+        v8i af[FM][NH], bf[NH], bnext;
+        vacc part[R];
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+        for (int r = 0; r < R; ++r) part[r] = vacc{};
+        // the "previous block" of the first block: zero partials times zero scales
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) sc[NST - 1].a[fm] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NSB; ++t) sc[NST - 1].b[t] = 0.f;
+
+        // This lane's byte offsets in a stage, made opaque to the compiler so that
+        // every fragment read is stage + offset + an immediate row offset instead
+        // of a separately hoisted address register per fragment and stage.  Only
+        // the offset is hidden: the stage array stays visible, so the compiler
+        // knows which stage a read touches and that it is not one the copies fill.
+        auto lane_base = [&](const uint8_t* smem, lds_u8* (&lb)[2][2]) {
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     int off = lsub * kKBlock + coff[h][e];
                     asm volatile("" : "+v"(off));
-                    lbase[h][e] = (lds_u8*)smem + off;
+                    lb[h][e] = (lds_u8*)smem + off;
                 }
-            // fragment of sub-tile rows [row0, row0+MF) for K half h (MF=16: whole block)
-            auto frag = [&](int row0, int h) -> v8i {
-                const v4i lo = *(const lds_v4i*)(lbase[h][0] + row0 * kKBlock);
-                const v4i hi = *(const lds_v4i*)(lbase[h][1] + row0 * kKBlock);
-                return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            };
-            constexpr int NH = MF == 32 ? 2 : 1;
-            v8i af[FM][NH];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int h = 0; h < NH; ++h) af[fm][h] = frag(wm * WTM + fm * MF, h);
-            v8i bf[NH], bnext[1];
-#pragma unroll
-            for (int h = 0; h < NH; ++h) bf[h] = frag(BM + wn * WTN, h);
-            bnext[0] = bf[0];
-            vacc part[kLag + 1];
-            // scale of sub-tile column fn for fragment row fm
-            float sbl = 0.f, sbh = 0.f;
-            if constexpr (MF == 16) {
-                sbl = uniform(sc.b[0]);
-                sbh = uniform(sc.b[NSB - 1]);
-            }
-            auto scale = [&](int fm, int fn) {
-                if constexpr (MF == 16) return sc.a[fm] * (((hi_mask >> fn) & 1u) ? sbh : sbl);
-                else return sc.a[fm] * sc.b[fn];
-            };
-            auto promote = [&](int j, int i0, int i1, float s) {
-                const int fn = j / FM, fm = j % FM;
-                const vacc& pj = part[j % (kLag + 1)];
-#pragma unroll
-                for (int i = i0; i < i1; ++i) acc[fm][fn][i] = __builtin_fmaf(pj[i], s, acc[fm][fn][i]);
-            };
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int fn = j / FM, fm = j % FM;
-                if constexpr (MF == 16) {
-                    if (fm == 0 && fn + 1 < FN) bnext[0] = frag(BM + wn * WTN + (fn + 1) * MF, 0);
-                    part[j % (kLag + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf[0], af[fm][0], vacc{}, 0, 0, 0, 0, 0, 0);
-                    if (j >= kLag) promote(j - kLag, 0, NACC, scale((j - kLag) % FM, (j - kLag) / FM));
-                    if (fm == FM - 1) bf[0] = bnext[0];
-                } else {
-                    // each K half's B fragment is reloaded for the next sub-tile column as
-                    // soon as the MFMA that reads it has been issued
-                    const bool reload = fm == FM - 1 && fn + 1 < FN;
-                    float s = 0.f;
-                    part[j % (kLag + 1)] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        bf[0], af[fm][0], vacc{}, 0, 0, 0, 0, 0, 0);
-                    if (reload) bf[0] = frag(BM + wn * WTN + (fn + 1) * MF, 0);
-                    if (j >= kLag) {
-                        s = scale((j - kLag) % FM, (j - kLag) / FM);
-                        promote(j - kLag, 0, NACC / 2, s);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    part[j % (kLag + 1)] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        bf[1], af[fm][1], part[j % (kLag + 1)], 0, 0, 0, 0, 0, 0);
-                    if (reload) bf[1] = frag(BM + wn * WTN + (fn + 1) * MF, 1);
-                    if (j >= kLag) promote(j - kLag, NACC / 2, NACC, s);
-                }
-#pragma unroll
-                for (int t = 0; t < NSLOT; ++t)
-                    if (j == t * NJ / NSLOT) issue_slot(nsmem, nkb, t);
-                if (j == NJ / 2) load_scales(sc_next, nkb);
-                // keep this order: the scheduler would otherwise pull each promotion up
-                // against its own MFMA and stall on the result
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int j = NJ - kLag; j < NJ; ++j) promote(j, 0, NACC, scale(j % FM, j / FM));
         };
+        // fragment of sub-tile rows [row0, row0+MF) for K half h (MF=16: whole block)
+        auto frag = [&](lds_u8* const (&lb)[2][2], int row0, int h) -> v8i {
+            const v4i lo = *(const lds_v4i*)(lb[h][0] + row0 * kKBlock);
+            const v4i hi = *(const lds_v4i*)(lb[h][1] + row0 * kKBlock);
+            return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        };
+        const int arow0 = wm * WTM, bcol0 = BM + wn * WTN;
 
-        // ---- K loop over NST LDS stages, unrolled by NST so every buffer is a named
-        // array.  Stage kb+NST-1's copies and scales are issued while block kb is
-        // consumed; before consuming block kb a wave waits only for its own loads of
-        // that block, leaving the younger stages' loads in flight. ----
-        constexpr int NVM = NSLOT + FM + NSB;      // vector memory instructions per stage
-        Scales sc[NST];
-        uint8_t* const stage_buf[4] = {smem0, smem1, smem2, smem3};
+        // ---- prologue: copies and scales of blocks 0 .. NST-2 (clamped), then the
+        // first block's fragments ----
 #pragma unroll
         for (int s = 0; s < NST - 1; ++s) {
             const int kk = s < KB ? s : KB - 1;
             load_scales(sc[s], kk);
             issue_stage(stage_buf[s], kk);
         }
-        for (int kb = 0; kb < KB; kb += NST) {
+        wait_vmem_le<(NST - 2) * NVM>();
+        stage_barrier();
+        if (wave_active) {
+            lds_u8* lb[2][2];
+            lane_base(smem0, lb);
 #pragma unroll
-            for (int u = 0; u < NST; ++u) {
-                if (kb + u >= KB) break;
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int h = 0; h < NH; ++h) af[fm][h] = frag(lb, arow0 + fm * MF, h);
+#pragma unroll
+            for (int h = 0; h < NH; ++h) bf[h] = frag(lb, bcol0, h);
+        }
+
+        // One K block (stage U of the unrolled loop, block index kbu).
+        auto block = [&](auto stage_tag, int kbu) {
+            constexpr int U = decltype(stage_tag)::value;
+            const uint8_t* cur = stage_buf[U];
+            const uint8_t* nxt = stage_buf[(U + 1) % NST];
+            uint8_t* dst = stage_buf[(U + NST - 1) % NST];
+            const Scales& scs = sc[U];
+            Scales& scp = sc[(U + NST - 1) % NST];   // previous block's; then reloaded
+            const int dkb = kbu + NST - 1 < KB ? kbu + NST - 1 : KB - 1;
+            lds_u8* lc[2][2];
+            lds_u8* ln[2][2];
+            lane_base(cur, lc);
+            lane_base(nxt, ln);
+            // B scales of this and of the previous block as scalars (MF=16: the wave's
+            // columns touch at most two scale rows, picked per column by hi_mask)
+            float cl = 0.f, ch = 0.f, pl = 0.f, ph = 0.f;
+            if constexpr (MF == 16) {
+                cl = uniform(scs.b[0]);
+                ch = uniform(scs.b[NSB - 1]);
+                pl = uniform(scp.b[0]);
+                ph = uniform(scp.b[NSB - 1]);
+            }
+            auto scale = [&](bool prev, int fm, int fn) {
+                const Scales& sc = prev ? scp : scs;
+                if constexpr (MF == 16) {
+                    const bool hi = (hi_mask >> fn) & 1u;
+                    return sc.a[fm] * (prev ? (hi ? ph : pl) : (hi ? ch : cl));
+                } else {
+                    return sc.a[fm] * sc.b[fn];
+                }
+            };
+            auto promote = [&](int q, int i0, int i1) {
+                // q: step index relative to this block, possibly negative (previous block)
+                const int slot = ((U * NJ + q) % R + R) % R;
+                const int qq = q < 0 ? q + NJ : q;
+                const float s = scale(q < 0, qq % FM, qq / FM);
+                const vacc& pq = part[slot];
+#pragma unroll
+                for (int i = i0; i < i1; ++i)
+                    acc[qq % FM][qq / FM][i] = __builtin_fmaf(pq[i], s, acc[qq % FM][qq / FM][i]);
+            };
+            auto issue_loads = [&](int j) {
+#pragma unroll
+                for (int t = 0; t < NSLOT; ++t)
+                    if (j == (t * SP < JB ? t * SP : JB)) issue_slot(dst, dkb, t);
+                if (j == JSC) load_scales(scp, dkb);
+            };
+            auto barrier = [&]() {
+                wait_lds_all();
                 wait_vmem_le<(NST - 2) * NVM>();
                 stage_barrier();
-                compute_stage(stage_buf[u], sc[u], stage_buf[(u + NST - 1) % NST], kb + u + NST - 1,
-                              sc[(u + NST - 1) % NST]);
+            };
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int fn = j / FM, fm = j % FM;
+                const int slot = (U * NJ + j) % R;
+                if constexpr (MF == 16) {
+                    part[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[0], af[fm][0], vacc{}, 0, 0,
+                                                                                  0, 0, 0, 0);
+                    promote(j - kLag, 0, NACC);
+                    issue_loads(j);
+                    if (j == JB) barrier();
+                    if (fm == 0) bnext = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 0) : frag(ln, bcol0, 0);
+                    if (fn == FN - 1) af[fm][0] = frag(ln, arow0 + fm * MF, 0);
+                    if (fm == FM - 1) bf[0] = bnext;
+                } else {
+                    part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[0], af[fm][0], vacc{}, 0, 0,
+                                                                                 0, 0, 0, 0);
+                    promote(j - kLag, 0, NACC / 2);
+                    issue_loads(j);
+                    if (j == JB) barrier();
+                    // each K half's fragments are reloaded as soon as the MFMA that
+                    // reads them for the last time in this block has been issued
+                    if (fm == FM - 1) bf[0] = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 0) : frag(ln, bcol0, 0);
+                    if (fn == FN - 1) af[fm][0] = frag(ln, arow0 + fm * MF, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[1], af[fm][1], part[slot], 0,
+                                                                                 0, 0, 0, 0, 0);
+                    promote(j - kLag, NACC / 2, NACC);
+                    if (fm == FM - 1) bf[1] = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 1) : frag(ln, bcol0, 1);
+                    if (fn == FN - 1) af[fm][1] = frag(ln, arow0 + fm * MF, 1);
+                }
+                // keep this order: the scheduler would otherwise pull each promotion up
+                // against its own MFMA and stall on the result
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // the partials of the last block's final kLag steps, promoted after the loop
+        auto drain = [&](auto stage_tag) {
+            constexpr int U = decltype(stage_tag)::value;
+            const Scales& sl = sc[U];
+#pragma unroll
+            for (int q = NJ - kLag; q < NJ; ++q) {
+                const int fm = q % FM, fn = q / FM;
+                float s;
+                if constexpr (MF == 16) s = sl.a[fm] * uniform(((hi_mask >> fn) & 1u) ? sl.b[NSB - 1] : sl.b[0]);
+                else s = sl.a[fm] * sl.b[fn];
+                const vacc& pq = part[(U * NJ + q) % R];
+#pragma unroll
+                for (int i = 0; i < NACC; ++i) acc[fm][fn][i] = __builtin_fmaf(pq[i], s, acc[fm][fn][i]);
+            }
+        };
+
+        if (wave_active) {
+            // whole groups of NST blocks, then the remaining KB % NST blocks: the hot
+            // loop has a single exit, which keeps the register allocator from
+            // splitting the accumulators' live ranges around mid-body exits
+            const int KF = KB - KB % NST;
+            for (int kb = 0; kb < KF; kb += NST) {
+                block(std::integral_constant<int, 0>{}, kb);
+                block(std::integral_constant<int, 1>{}, kb + 1);
+                if constexpr (NST > 2) block(std::integral_constant<int, 2 % NST>{}, kb + 2);
+                if constexpr (NST > 3) block(std::integral_constant<int, 3 % NST>{}, kb + 3);
+            }
+            if constexpr (NST > 1) {
+                if (KF < KB) block(std::integral_constant<int, 0>{}, KF);
+            }
+            if constexpr (NST > 2) {
+                if (KF + 1 < KB) block(std::integral_constant<int, 1>{}, KF + 1);
+            }
+            if constexpr (NST > 3) {
+                if (KF + 2 < KB) block(std::integral_constant<int, 2 % NST>{}, KF + 2);
+            }
+            const int ul = (KB - 1) % NST;
+            if (ul == 0) drain(std::integral_constant<int, 0>{});
+            if (ul == 1) drain(std::integral_constant<int, 1>{});
+            if constexpr (NST > 2) if (ul == 2) drain(std::integral_constant<int, 2 % NST>{});
+            if constexpr (NST > 3) if (ul == 3) drain(std::integral_constant<int, 3 % NST>{});
+        } else {
+            // a wave with no valid rows (masked / short tiles) still copies its share
+            // of every stage and meets every barrier; it loads no scales, so it waits
+            // for its copies alone
+            for (int kb = 0; kb < KB; kb += NST) {
+#pragma unroll
+                for (int u = 0; u < NST; ++u) {
+                    if (kb + u >= KB) break;
+                    const int dkb = kb + u + NST - 1 < KB ? kb + u + NST - 1 : KB - 1;
+                    issue_stage(stage_buf[(u + NST - 1) % NST], dkb);
+                    wait_vmem_le<(NST - 2) * NSLOT>();
+                    stage_barrier();
+                }
             }
         }
 
