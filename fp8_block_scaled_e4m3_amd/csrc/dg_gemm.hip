@@ -46,6 +46,7 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) const v4i lds_v4i;
+typedef __attribute__((address_space(3))) const float lds_f32;
 
 constexpr int kKBlock = 128;        // K bytes per scale block == K of one MFMA
 constexpr int kMaxMaskedGroups = 1024;
@@ -110,13 +111,16 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int NACC = MF * MF / 64;             // accumulator floats per lane per sub-tile
     constexpr int ROWS = BM + BN;
-    constexpr int STAGE = ROWS * kKBlock;
+    // a stage holds the block's operand rows and, behind them, each wave's copy of
+    // the A scales of its rows (64 fp32 values per wave)
+    constexpr int STAGE = ROWS * kKBlock + NW * 256;
     constexpr int A_SLOTS = BM / 8, B_SLOTS = BN / 8;
     constexpr int A_PER = (A_SLOTS + NW - 1) / NW, B_PER = (B_SLOTS + NW - 1) / NW;
     static_assert(MF == 16 || MF == 32, "matrix instruction shape");
     static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "block rows must be a multiple of 8");
     static_assert(WTN <= 256, "a wave's columns touch at most three B scale blocks");
+    static_assert(WTM <= 64, "one 4-byte-per-lane copy carries a wave's A scales");
     typedef float vacc __attribute__((ext_vector_type(NACC)));
 
     // NST stage buffers, each its own array so the compiler can prove that fragment
@@ -270,13 +274,14 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             for (int t = 0; t < NSLOT; ++t) issue_slot(smem, kb, t);
         };
 
-        // ---- per-lane scale sources ----
-        uint32_t sa_off[FM];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int r = wm * WTM + fm * MF + lsub;
-            sa_off[fm] = (uint32_t)(r > a_last ? a_last : r) * 4u;
-        }
+        // ---- scale sources ----
+        // A scales: a wave's rows of a K block are contiguous in sA (MN-major), so they
+        // travel to LDS with the block's operands, one 4-byte copy per lane (row
+        // wm*WTM + lane) into the wave's own 256-byte area of the stage.  The K offset
+        // is in the per-lane offset, which the descriptor bounds (rows past the end of
+        // sA read zeros).
+        const uint32_t sa_voff = (uint32_t)(wm * WTM + lane) * 4u;
+        const int sa_lds = ROWS * kKBlock + wave * 256 + lsub * 4;   // this lane's row, sub-tile 0
         // Sub-tile column fn (MF columns, inside one 128-column scale block because MF
         // divides 128 and the column offsets are multiples of MF) reads its B scales
         // from row nb(fn) of sB; the byte offset of that row is wave-uniform.
@@ -299,7 +304,6 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 sb_off[fn] = min((wcol0 + fn * MF) / kKBlock, p.nblocks - 1) * KB * 4;
         }
         const __amdgpu_buffer_rsrc_t rs_sa = make_rsrc(sa_tile, ((long)KB * p.ld_sa - m0) * 4);
-        const __amdgpu_buffer_rsrc_t rs_sb = make_rsrc(sb_grp, (long)p.nblocks * KB * 4);
         const bool wave_active = wm * WTM < valid_rows;
 
         vacc acc[FM][FN];
@@ -318,13 +322,33 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             for (int e = 0; e < 2; ++e)
                 coff[h][e] = (((MF == 16 ? 2 * lgrp : 4 * h + 2 * lgrp) + e) ^ swz(lane & 15)) * 16;
 
+        // Scales of one K block: a[fm] per lane (its row of sub-tile row fm), b[t]
+        // wave-uniform (scalar loads of sB, which never pass through the texture unit)
         struct Scales { float a[FM]; float b[NSB]; };
-        auto load_scales = [&](Scales& sc, int kb) {
-            const int soff = kb * p.ld_sa * 4;
+        auto issue_sa = [&](uint8_t* smem, int kb) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_sa, (lds_void*)(smem + ROWS * kKBlock + wave * 256), 4,
+                                                     (int)(sa_voff + (uint32_t)(kb * p.ld_sa) * 4u), 0, 0, 0);
+        };
+        auto load_sb = [&](Scales& sc, int kb) {
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) sc.a[fm] = load_f32(rs_sa, (int)sa_off[fm], soff);
+            for (int t = 0; t < NSB; ++t) sc.b[t] = sb_grp[(sb_off[t] >> 2) + kb];
+        };
+        auto read_sa = [&](Scales& sc, const uint8_t* smem) {
 #pragma unroll
-            for (int t = 0; t < NSB; ++t) sc.b[t] = load_f32(rs_sb, 0, sb_off[t] + kb * 4);
+            for (int fm = 0; fm < FM; ++fm)
+                sc.a[fm] = *(const lds_f32*)((const lds_u8*)smem + sa_lds + fm * MF * 4);
+        };
+        // the B scale of sub-tile column fn as a scalar: MF=16 picks the wave's low or
+        // high scale row with uniform integer operations
+        auto pick_b = [&](const Scales& sc, int fn) -> float {
+            if constexpr (MF == 16) {
+                const unsigned m = 0u - ((hi_mask >> fn) & 1u);
+                const unsigned lo = __builtin_bit_cast(unsigned, sc.b[0]);
+                const unsigned hi = __builtin_bit_cast(unsigned, sc.b[NSB - 1]);
+                return __builtin_bit_cast(float, lo ^ ((lo ^ hi) & m));
+            } else {
+                return sc.b[fn];
+            }
         };
 
         // ---- K loop: one continuous stream of steps over (K block, column fn, row fm).
@@ -350,10 +374,10 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                         : ((NST * NJ) % 4 == 0 ? 4 : ((NST * NJ) % 3 == 0 ? 3 : 2));
         static_assert((NST * NJ) % R == 0, "partial ring must tile the unrolled loop");
         constexpr int kLag = R - 1;
-        constexpr int NVM = NSLOT + FM + NSB;      // vector memory instructions per block
+        constexpr int NVM = NSLOT + 1;             // vector memory instructions per block
         // copy slot t is issued at step jslot(t), all of them no later than step JB
         constexpr int SP = (JB + 1) / (2 * NSLOT) > 1 ? (JB + 1) / (2 * NSLOT) : 1;
-        constexpr int JSC = kLag < JB ? kLag : JB; // scale loads of block kb + NST - 1
+        constexpr int JSC = kLag < JB ? kLag : JB; // B-scale loads of the next block
 
         Scales sc[NST];
         uint8_t* const stage_buf[4] = {smem0, smem1, smem2, smem3};
@@ -391,17 +415,19 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         };
         const int arow0 = wm * WTM, bcol0 = BM + wn * WTN;
 
-        // ---- prologue: copies and scales of blocks 0 .. NST-2 (clamped), then the
-        // first block's fragments ----
+        // ---- prologue: copies of blocks 0 .. NST-2 (clamped), then the first
+        // block's fragments and scales ----
 #pragma unroll
         for (int s = 0; s < NST - 1; ++s) {
             const int kk = s < KB ? s : KB - 1;
-            load_scales(sc[s], kk);
             issue_stage(stage_buf[s], kk);
+            issue_sa(stage_buf[s], kk);
         }
         wait_vmem_le<(NST - 2) * NVM>();
         stage_barrier();
         if (wave_active) {
+            load_sb(sc[0], 0);
+            read_sa(sc[0], smem0);
             lds_u8* lb[2][2];
             lane_base(smem0, lb);
 #pragma unroll
@@ -419,29 +445,17 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             const uint8_t* nxt = stage_buf[(U + 1) % NST];
             uint8_t* dst = stage_buf[(U + NST - 1) % NST];
             const Scales& scs = sc[U];
-            Scales& scp = sc[(U + NST - 1) % NST];   // previous block's; then reloaded
+            const Scales& scp = sc[(U + NST - 1) % NST];   // previous block's
+            Scales& scn = sc[(U + 1) % NST];               // next block's (for NST=2: scp's slot)
             const int dkb = kbu + NST - 1 < KB ? kbu + NST - 1 : KB - 1;
+            const int nkb = kbu + 1 < KB ? kbu + 1 : KB - 1;
             lds_u8* lc[2][2];
             lds_u8* ln[2][2];
             lane_base(cur, lc);
             lane_base(nxt, ln);
-            // B scales of this and of the previous block as scalars (MF=16: the wave's
-            // columns touch at most two scale rows, picked per column by hi_mask)
-            float cl = 0.f, ch = 0.f, pl = 0.f, ph = 0.f;
-            if constexpr (MF == 16) {
-                cl = uniform(scs.b[0]);
-                ch = uniform(scs.b[NSB - 1]);
-                pl = uniform(scp.b[0]);
-                ph = uniform(scp.b[NSB - 1]);
-            }
             auto scale = [&](bool prev, int fm, int fn) {
                 const Scales& sc = prev ? scp : scs;
-                if constexpr (MF == 16) {
-                    const bool hi = (hi_mask >> fn) & 1u;
-                    return sc.a[fm] * (prev ? (hi ? ph : pl) : (hi ? ch : cl));
-                } else {
-                    return sc.a[fm] * sc.b[fn];
-                }
+                return sc.a[fm] * pick_b(sc, fn);
             };
             auto promote = [&](int q, int i0, int i1) {
                 // q: step index relative to this block, possibly negative (previous block)
@@ -457,7 +471,10 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
 #pragma unroll
                 for (int t = 0; t < NSLOT; ++t)
                     if (j == (t * SP < JB ? t * SP : JB)) issue_slot(dst, dkb, t);
-                if (j == JSC) load_scales(scp, dkb);
+                if (j == 0) issue_sa(dst, dkb);
+                // the next block's B scales; the slot's previous contents were last
+                // used by the promotions of the steps before JSC
+                if (j == JSC) load_sb(scn, nkb);
             };
             auto barrier = [&]() {
                 wait_lds_all();
@@ -475,6 +492,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                     issue_loads(j);
                     if (j == JB) barrier();
                     if (fm == 0) bnext = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 0) : frag(ln, bcol0, 0);
+                    if (j == JB) read_sa(scn, nxt);
                     if (fn == FN - 1) af[fm][0] = frag(ln, arow0 + fm * MF, 0);
                     if (fm == FM - 1) bf[0] = bnext;
                 } else {
@@ -486,6 +504,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                     // each K half's fragments are reloaded as soon as the MFMA that
                     // reads them for the last time in this block has been issued
                     if (fm == FM - 1) bf[0] = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 0) : frag(ln, bcol0, 0);
+                    if (j == JB) read_sa(scn, nxt);
                     if (fn == FN - 1) af[fm][0] = frag(ln, arow0 + fm * MF, 0);
                     __builtin_amdgcn_sched_barrier(0);
                     part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[1], af[fm][1], part[slot], 0,
@@ -506,9 +525,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
 #pragma unroll
             for (int q = NJ - kLag; q < NJ; ++q) {
                 const int fm = q % FM, fn = q / FM;
-                float s;
-                if constexpr (MF == 16) s = sl.a[fm] * uniform(((hi_mask >> fn) & 1u) ? sl.b[NSB - 1] : sl.b[0]);
-                else s = sl.a[fm] * sl.b[fn];
+                const float s = sl.a[fm] * pick_b(sl, fn);
                 const vacc& pq = part[(U * NJ + q) % R];
 #pragma unroll
                 for (int i = 0; i < NACC; ++i) acc[fm][fn][i] = __builtin_fmaf(pq[i], s, acc[fm][fn][i]);
@@ -542,15 +559,15 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             if constexpr (NST > 3) if (ul == 3) drain(std::integral_constant<int, 3 % NST>{});
         } else {
             // a wave with no valid rows (masked / short tiles) still copies its share
-            // of every stage and meets every barrier; it loads no scales, so it waits
-            // for its copies alone
+            // of every stage (operands and A scales) and meets every barrier
             for (int kb = 0; kb < KB; kb += NST) {
 #pragma unroll
                 for (int u = 0; u < NST; ++u) {
                     if (kb + u >= KB) break;
                     const int dkb = kb + u + NST - 1 < KB ? kb + u + NST - 1 : KB - 1;
                     issue_stage(stage_buf[(u + NST - 1) % NST], dkb);
-                    wait_vmem_le<(NST - 2) * NSLOT>();
+                    issue_sa(stage_buf[(u + NST - 1) % NST], dkb);
+                    wait_vmem_le<(NST - 2) * NVM>();
                     stage_barrier();
                 }
             }
