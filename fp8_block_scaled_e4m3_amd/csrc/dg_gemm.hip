@@ -375,9 +375,21 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         static_assert((NST * NJ) % R == 0, "partial ring must tile the unrolled loop");
         constexpr int kLag = R - 1;
         constexpr int NVM = NSLOT + 1;             // vector memory instructions per block
-        // copy slot t is issued at step jslot(t), all of them no later than step JB
-        constexpr int SP = (JB + 1) / (2 * NSLOT) > 1 ? (JB + 1) / (2 * NSLOT) : 1;
-        constexpr int JSC = kLag < JB ? kLag : JB; // B-scale loads of the next block
+        // Copies of block kb + NST (NSLOT operand slots, then the A-scale copy) go to
+        // stage kb % NST as soon as block kb's barrier has freed it: copy t at step
+        // JB + 1 + t*CPN/CPD of block kb (two steps apart when a block is long enough),
+        // running on into the first steps of block kb+1, never past its barrier
+        // (where, for NST=2, they must have landed).
+        constexpr int NDMA = NSLOT + 1;
+        constexpr int CPN = 2 * NDMA + 4 <= NJ ? 2 : (NDMA + 4 <= NJ ? 1 : NJ);
+        constexpr int CPD = CPN == NJ ? NDMA : 1;
+        static_assert((NDMA - 1) * CPN / CPD + 1 <= NJ, "copies must be issued before the next barrier");
+        constexpr int NFIRST = [] {   // copies issued in the freeing block
+            int c = 0;
+            for (int t = 0; t < NDMA; ++t) c += JB + 1 + t * CPN / CPD < NJ;
+            return c;
+        }();
+        static_assert(kLag <= JB, "the previous block's scales are dead by the barrier");
 
         Scales sc[NST];
         uint8_t* const stage_buf[4] = {smem0, smem1, smem2, smem3};
@@ -415,27 +427,38 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         };
         const int arow0 = wm * WTM, bcol0 = BM + wn * WTN;
 
-        // ---- prologue: copies of blocks 0 .. NST-2 (clamped), then the first
-        // block's fragments and scales ----
+        auto issue_copy = [&](int t, uint8_t* smem, int kb) {
+            kb = kb < KB ? kb : KB - 1;
+            if (t < NSLOT) issue_slot(smem, kb, t);
+            else issue_sa(smem, kb);
+        };
+        // ---- prologue: copies of blocks 0 .. NST-2 and the early part of block
+        // NST-1's (all clamped), then the first block's fragments and scales ----
 #pragma unroll
         for (int s = 0; s < NST - 1; ++s) {
             const int kk = s < KB ? s : KB - 1;
             issue_stage(stage_buf[s], kk);
             issue_sa(stage_buf[s], kk);
         }
-        wait_vmem_le<(NST - 2) * NVM>();
+#pragma unroll
+        for (int t = 0; t < NFIRST; ++t) issue_copy(t, stage_buf[NST - 1], NST - 1);
+        // (the scalar loads complete before the loop, so the loop starts with only LDS
+        // reads in flight, in the order the loop itself issues them: B fragment, A
+        // scales, A fragments)
+        if (wave_active) load_sb(sc[0], 0);
+        wait_lds_all();
+        wait_vmem_le<(NST - 2) * NVM + NFIRST>();
         stage_barrier();
         if (wave_active) {
-            load_sb(sc[0], 0);
-            read_sa(sc[0], smem0);
             lds_u8* lb[2][2];
             lane_base(smem0, lb);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
+            for (int h = 0; h < NH; ++h) {
+                bf[h] = frag(lb, bcol0, h);
+                if (h == 0) read_sa(sc[0], smem0);
 #pragma unroll
-                for (int h = 0; h < NH; ++h) af[fm][h] = frag(lb, arow0 + fm * MF, h);
-#pragma unroll
-            for (int h = 0; h < NH; ++h) bf[h] = frag(lb, bcol0, h);
+                for (int fm = 0; fm < FM; ++fm) af[fm][h] = frag(lb, arow0 + fm * MF, h);
+            }
         }
 
         // One K block (stage U of the unrolled loop, block index kbu).
@@ -447,7 +470,6 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             const Scales& scs = sc[U];
             const Scales& scp = sc[(U + NST - 1) % NST];   // previous block's
             Scales& scn = sc[(U + 1) % NST];               // next block's (for NST=2: scp's slot)
-            const int dkb = kbu + NST - 1 < KB ? kbu + NST - 1 : KB - 1;
             const int nkb = kbu + 1 < KB ? kbu + 1 : KB - 1;
             lds_u8* lc[2][2];
             lds_u8* ln[2][2];
@@ -469,14 +491,19 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             };
             auto issue_loads = [&](int j) {
 #pragma unroll
-                for (int t = 0; t < NSLOT; ++t)
-                    if (j == (t * SP < JB ? t * SP : JB)) issue_slot(dst, dkb, t);
-                if (j == 0) issue_sa(dst, dkb);
-                // the next block's B scales; the slot's previous contents were last
-                // used by the promotions of the steps before JSC
-                if (j == JSC) load_sb(scn, nkb);
+                for (int t = 0; t < NDMA; ++t) {
+                    const int g = JB + 1 + t * CPN / CPD;
+                    if (g < NJ && j == g) issue_copy(t, stage_buf[U], kbu + NST);
+                    if (g >= NJ && j == g - NJ) issue_copy(t, dst, kbu + NST - 1);
+                }
             };
             auto barrier = [&]() {
+                // The next block's B scales (scalar loads) are issued here, where the
+                // wave waits for all its LDS reads anyway: scalar loads complete out of
+                // order and share that counter, so while one is in flight every wait
+                // for an LDS read would have to be a wait for all of them.  The slot's
+                // previous contents were last used by promotions early in this block.
+                load_sb(scn, nkb);
                 wait_lds_all();
                 wait_vmem_le<(NST - 2) * NVM>();
                 stage_barrier();
