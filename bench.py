@@ -139,6 +139,43 @@ def cpu_baseline(w, data, target_s: float):
                       f"on {cores} host threads"}
 
 
+CASTS = (("cast_1x128_m4096_k7168_f32", 4096, 7168, 1),
+         ("cast_128x128_n7168_k7168_f32", 7168, 7168, 128))
+
+
+def time_casts(iters, flush):
+    """The FP8 casts that feed the GEMM (fp32 in, E4M3 + scales out): HBM-bound."""
+    import torch
+
+    import fp8_block_scaled_e4m3_amd as dg
+    import workloads as W
+    from tests.gpu_support import say
+
+    out = {}
+    for cname, rows, k, gran in CASTS:
+        say(f"bench: cast {cname}")
+        x = torch.from_numpy(W.make_fp32_operand(rows, k, gran, seed=0)).to("cuda:0")
+        q = torch.empty((rows, k), dtype=torch.uint8, device="cuda:0")
+        if gran == 1:
+            s_ = torch.empty((k // 128, W.ld_sa_for(rows)), device="cuda:0")
+            c3 = lambda: dg.dg_quantize_fp8_1x128(x, q, s_)
+            nsc = (k // 128) * rows
+        else:
+            s_ = torch.empty((ceil_div(rows, 128), k // 128), device="cuda:0")
+            c3 = lambda: dg.dg_quantize_fp8_128x128(x, q, s_)
+            nsc = ceil_div(rows, 128) * (k // 128)
+        b3 = rows * k * 4 + rows * k + 4 * nsc
+        for _ in range(3):
+            c3()
+        mean_s, _ = time_launches(c3, iters, flush)
+        out[cname] = {"us": round(mean_s * 1e6, 2), "gbps": round(b3 / mean_s / 1e9, 1),
+                      "frac_hbm": round(b3 / mean_s / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm",
+                      "caches_flushed": True, "algorithmic_bytes": b3, "traffic": traffic_for(cname)}
+        del x, q, s_, c3
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +186,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--secondary-iters", type=int, default=20)
+    ap.add_argument("--only-casts", action="store_true",
+                    help="only time the two FP8 cast kernels (used for their profiles)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -168,6 +207,10 @@ def main():
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     dg.load_library()
+    if args.only_casts:
+        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+        print(json.dumps({"casts": time_casts(args.secondary_iters, flush)}), flush=True)
+        return
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20
         src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
@@ -270,29 +313,7 @@ def main():
                 sec[name]["sum_masked_m"] = int(np.clip(d2["masked_m"], 0, ww.max_m).sum())
             del d2, v2, o2, c2
             torch.cuda.empty_cache()
-        # the FP8 cast that feeds the GEMM (fp32 in, E4M3 + scales out): HBM-bound
-        for cname, rows, k, gran in (("cast_1x128_m4096_k7168_f32", 4096, 7168, 1),
-                                     ("cast_128x128_n7168_k7168_f32", 7168, 7168, 128)):
-            say(f"bench: secondary {cname}")
-            x = torch.from_numpy(W.make_fp32_operand(rows, k, gran, seed=0)).to("cuda:0")
-            q = torch.empty((rows, k), dtype=torch.uint8, device="cuda:0")
-            if gran == 1:
-                s_ = torch.empty((k // 128, W.ld_sa_for(rows)), device="cuda:0")
-                c3 = lambda: dg.dg_quantize_fp8_1x128(x, q, s_)
-                nsc = (k // 128) * rows
-            else:
-                s_ = torch.empty((ceil_div(rows, 128), k // 128), device="cuda:0")
-                c3 = lambda: dg.dg_quantize_fp8_128x128(x, q, s_)
-                nsc = ceil_div(rows, 128) * (k // 128)
-            b3 = rows * k * 4 + rows * k + 4 * nsc
-            for _ in range(3):
-                c3()
-            mean_s, _ = time_launches(c3, args.secondary_iters, flush)
-            sec[cname] = {"us": round(mean_s * 1e6, 2), "gbps": round(b3 / mean_s / 1e9, 1),
-                          "frac_hbm": round(b3 / mean_s / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm",
-                          "caches_flushed": True, "algorithmic_bytes": b3, "traffic": traffic_for(cname)}
-            del x, q, s_, c3
-            torch.cuda.empty_cache()
+        sec.update(time_casts(args.secondary_iters, flush))
         result["secondary"] = sec
 
     if not args.no_cpu_baseline and w.kind == "dense":
