@@ -91,7 +91,9 @@ def time_launches(call, iters, flush=None):
     pairs = []
     for _ in range(iters):
         if flush is not None:
-            flush.add_(1)                     # evict L2 and the Infinity Cache
+            # evict L2 and the Infinity Cache by reading 512 MB: a read leaves the
+            # caches clean, so the timed kernel pays for no write-back of the flush
+            flush.amax()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record(stream)
         call()
@@ -208,7 +210,7 @@ def main():
         raise RuntimeError("bench.py needs a GPU")
     dg.load_library()
     if args.only_casts:
-        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+        flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
         print(json.dumps({"casts": time_casts(args.secondary_iters, flush)}), flush=True)
         return
     if args.copy_calibration_mib:
@@ -288,7 +290,7 @@ def main():
 
     if not args.no_secondary:
         sec = {}
-        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+        flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
         for name, ww in W.WORKLOADS.items():
             if name == w.name or name.startswith("dense_m128"):
                 continue

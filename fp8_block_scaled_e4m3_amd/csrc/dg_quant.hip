@@ -46,64 +46,122 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
     return sign | ((rounded >> 20) - (120u << 3));     // rebias exponent 127 -> 7
 }
 
-// 16 lanes per (row, K block): each lane owns 8 consecutive elements.
+// One 16-byte load: 4 fp32 or 8 bf16 values, widened to fp32 (bf16 -> fp32 is exact).
+template <typename T> struct Vec;
+template <> struct Vec<float> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ void load(const float* p, float* v) {
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        const f4 t = __builtin_nontemporal_load((const f4*)p);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    }
+};
+template <> struct Vec<uint16_t> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ void load(const uint16_t* p, float* v) {
+        typedef unsigned u4 __attribute__((ext_vector_type(4)));
+        const u4 t = __builtin_nontemporal_load((const u4*)p);
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+};
+
+__device__ __forceinline__ float amax_of(const float* v, int n, float amax) {
+    for (int i = 0; i < n; ++i) {
+        const float m = fabsf(v[i]);
+        amax = m > amax ? m : amax;              // a NaN never raises the maximum
+    }
+    return amax;
+}
+
+// N codes of v / scale packed little-endian (4 -> one dword, 8 -> two)
+template <int N>
+__device__ __forceinline__ void store_codes(uint8_t* dst, const float* v, float scale) {
+    uint32_t w[N / 4];
+#pragma unroll
+    for (int d = 0; d < N / 4; ++d) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c |= e4m3_code(v[4 * d + e] / scale) << (8 * e);
+        w[d] = c;
+    }
+    if constexpr (N == 4) *(uint32_t*)dst = w[0];
+    else *(uint2*)dst = uint2{w[0], w[1]};
+}
+
+// 1x128: a 128-element row block is read by L = 128/N lanes with one 16-byte load
+// each (the block's bytes are contiguous, so every load instruction is coalesced).
+// A thread handles kRowsPerThread row blocks of one K block, their loads all in
+// flight before any is reduced.  Blocks are numbered K block fastest, so a
+// workgroup reads long contiguous stretches of each row.
+constexpr int kRowsPerThread = 4;
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, uint8_t* __restrict__ q, long ldq,
                    float* __restrict__ sa, long ld_sa) {
-    const long blk = ((long)blockIdx.x * 256 + threadIdx.x) >> 4;   // row fastest
-    if (blk >= (long)rows * kblocks) return;                         // whole 16-lane groups
-    const int l16 = threadIdx.x & 15;
-    const int row = (int)(blk % rows), kb = (int)(blk / rows);
-    const long k0 = (long)kb * kQBlock + l16 * 8;
-    const T* src = x + (long)row * ldx + k0;
-    float v[8];
+    constexpr int N = Vec<T>::N, L = kQBlock / N, GPW = 256 / L;   // groups of L lanes per workgroup
+    const int lg = threadIdx.x % L, grp = threadIdx.x / L;
+    // workgroup w handles groups [w*GPW*R, (w+1)*GPW*R); group g = (row, kb) with kb
+    // fastest (the host keeps rows * kblocks below 2^31)
+    const unsigned groups_total = (unsigned)rows * (unsigned)kblocks;
+    const unsigned g0 = blockIdx.x * (unsigned)(GPW * kRowsPerThread) + grp;
+    float v[kRowsPerThread][N];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = load_elem(src + i);
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float m = fabsf(v[i]);
-        amax = m > amax ? m : amax;
+    for (int r = 0; r < kRowsPerThread; ++r) {
+        const unsigned g = g0 + r * GPW;
+        if (g < groups_total) {
+            const unsigned row = g / (unsigned)kblocks, kb = g - row * (unsigned)kblocks;
+            Vec<T>::load(x + (long)row * ldx + kb * kQBlock + lg * N, v[r]);
+        }
     }
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-        const float o = __shfl_xor(amax, off, 16);
-        amax = o > amax ? o : amax;
+    for (int r = 0; r < kRowsPerThread; ++r) {
+        const unsigned g = g0 + r * GPW;
+        if (g >= groups_total) break;                   // uniform over the L lanes of a group
+        float amax = amax_of(v[r], N, 0.f);
+#pragma unroll
+        for (int off = L / 2; off >= 1; off >>= 1) {
+            const float o = __shfl_xor(amax, off, L);
+            amax = o > amax ? o : amax;
+        }
+        const float scale = amax == 0.f ? 1.f : amax / kE4M3Max;
+        const unsigned row = g / (unsigned)kblocks, kb = g - row * (unsigned)kblocks;
+        store_codes<N>(q + (long)row * ldq + kb * kQBlock + lg * N, v[r], scale);
+        if (lg == 0) sa[(long)kb * ld_sa + row] = scale;
     }
-    const float scale = amax == 0.f ? 1.f : amax / kE4M3Max;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_code(v[i] / scale) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_code(v[4 + i] / scale) << (8 * i);
-    *(uint2*)(q + (long)row * ldq + k0) = uint2{lo, hi};
-    if (l16 == 0) sa[(long)kb * ld_sa + row] = scale;
 }
 
-// One workgroup per 128x128 block: thread t owns row t/2, columns (t%2)*64 .. +63.
+// 128x128: one workgroup per block.  Every load instruction of the workgroup reads
+// whole 512-byte (fp32) or 256-byte (bf16) row segments: lane t of a pass covers
+// row pass*RPP + t/L, columns (t%L)*N .. +N.  All passes' loads are in flight
+// before the reduction.
 template <typename T>
 __global__ void __launch_bounds__(256)
 quant_128x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, uint8_t* __restrict__ q, long ldq,
                      float* __restrict__ sb) {
+    constexpr int N = Vec<T>::N, L = kQBlock / N, RPP = 256 / L, PASSES = kQBlock / RPP;
     __shared__ float s_amax[4];
     const int kb = blockIdx.x, rb = blockIdx.y;
     const int t = threadIdx.x;
-    const int row = rb * kQBlock + (t >> 1);
-    const long c0 = (long)kb * kQBlock + (t & 1) * 64;
-    const bool live = row < rows;
-    float v[64];
+    const int r0 = rb * kQBlock + t / L;
+    const long c0 = (long)kb * kQBlock + (t % L) * N;
+    float v[PASSES][N];
     float amax = 0.f;
-    if (live) {
-        const T* src = x + (long)row * ldx + c0;
 #pragma unroll
-        for (int i = 0; i < 64; ++i) v[i] = load_elem(src + i);
+    for (int i = 0; i < PASSES; ++i) {
+        const int row = r0 + i * RPP;
+        if (row < rows) Vec<T>::load(x + (long)row * ldx + c0, v[i]);
+        else
 #pragma unroll
-        for (int i = 0; i < 64; ++i) {
-            const float m = fabsf(v[i]);
-            amax = m > amax ? m : amax;
-        }
+            for (int e = 0; e < N; ++e) v[i][e] = 0.f;
     }
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) amax = amax_of(v[i], N, amax);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const float o = __shfl_xor(amax, off, 64);
@@ -116,16 +174,10 @@ quant_128x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, u
     for (int w = 1; w < 4; ++w) amax = s_amax[w] > amax ? s_amax[w] : amax;
     const float scale = amax == 0.f ? 1.f : amax / kE4M3Max;
     if (t == 0) sb[(long)rb * kblocks + kb] = scale;
-    if (!live) return;
-    uint8_t* dst = q + (long)row * ldq + c0;
 #pragma unroll
-    for (int i = 0; i < 64; i += 8) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lo |= e4m3_code(v[i + e] / scale) << (8 * e);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hi |= e4m3_code(v[i + 4 + e] / scale) << (8 * e);
-        *(uint2*)(dst + i) = uint2{lo, hi};
+    for (int i = 0; i < PASSES; ++i) {
+        const int row = r0 + i * RPP;
+        if (row < rows) store_codes<N>(q + (long)row * ldq + c0, v[i], scale);
     }
 }
 
@@ -134,15 +186,24 @@ quant_128x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, u
 hipError_t launch_quant_1x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq, float* sa,
                               long ld_sa, hipStream_t stream) {
     const int kblocks = k / kQBlock;
-    const long groups = (long)rows * kblocks;
-    const long blocks = (groups * 16 + 255) / 256;
-    if (x_bf16)
-        hipLaunchKernelGGL(quant_1x128_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(x), ldx, rows, kblocks, q, ldq, sa, ld_sa);
-    else
-        hipLaunchKernelGGL(quant_1x128_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           static_cast<const float*>(x), ldx, rows, kblocks, q, ldq, sa, ld_sa);
-    return hipGetLastError();
+    const long per_wg = (x_bf16 ? 256 / 16 : 256 / 32) * (long)kRowsPerThread;   // groups per workgroup
+    // row chunks small enough for 32-bit group indices inside the kernel
+    const long chunk = ((1l << 30) / kblocks) > 0 ? ((1l << 30) / kblocks) : 1;
+    for (long r0 = 0; r0 < rows; r0 += chunk) {
+        const int nr = (int)(rows - r0 < chunk ? rows - r0 : chunk);
+        const long blocks = ((long)nr * kblocks + per_wg - 1) / per_wg;
+        if (x_bf16)
+            hipLaunchKernelGGL(quant_1x128_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                               static_cast<const uint16_t*>(x) + r0 * ldx, ldx, nr, kblocks, q + r0 * ldq, ldq,
+                               sa + r0, ld_sa);
+        else
+            hipLaunchKernelGGL(quant_1x128_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                               static_cast<const float*>(x) + r0 * ldx, ldx, nr, kblocks, q + r0 * ldq, ldq, sa + r0,
+                               ld_sa);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_quant_128x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq,
