@@ -600,10 +600,18 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             }
         }
 
-        // ---- epilogue: BF16 RNE, 8-byte stores, skip padding / masked / tail rows.
-        // A lane owns row lsub of each sub-tile and runs of four adjacent columns:
-        // MF=16: columns 4g..4g+3; MF=32: columns 8q+4g..8q+4g+3, q = 0..3. ----
+        // ---- epilogue: BF16 RNE, skip padding / masked / tail rows.  A lane owns row
+        // lsub of each sub-tile and runs of four adjacent columns (MF=16: columns
+        // 4g..4g+3 of lane group g; MF=32: columns 8q+4g..8q+4g+3, q = 0..3).  MF=16:
+        // for each pair of sub-tile columns, two lane-group swaps (V_PERMLANE16_SWAP)
+        // give every lane eight adjacent columns of one sub-tile, so a store
+        // instruction writes 64 contiguous bytes per row in 16-byte pieces. ----
         if (wave_active) {
+            auto pack2 = [](float x, float y) -> uint32_t {
+                typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+                const v2bf t = {(__bf16)x, (__bf16)y};
+                return __builtin_bit_cast(uint32_t, t);
+            };
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
                 const int lr = wm * WTM + fm * MF + lsub;     // row inside the tile
@@ -611,20 +619,35 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 if constexpr (LAYOUT == kContiguous) {
                     if (row_ok) row_ok = p.m_indices[m0 + lr] >= 0;
                 }
-                if (!row_ok) continue;
-                uint16_t* drow = d_base + (long)(m0 + lr) * p.ldd;
+                uint16_t* drow = d_base + (long)(m0 + (row_ok ? lr : 0)) * p.ldd;
+                if constexpr (MF == 16) {
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
+                    for (int fn = 0; fn + 1 < FN; fn += 2) {
+                        const vacc& x = acc[fm][fn];
+                        const vacc& y = acc[fm][fn + 1];
+                        // every lane takes part in the swaps; only the stores are predicated
+                        const auto s0 = __builtin_amdgcn_permlane16_swap(pack2(x[0], x[1]), pack2(y[0], y[1]), false,
+                                                                         false);
+                        const auto s1 = __builtin_amdgcn_permlane16_swap(pack2(x[2], x[3]), pack2(y[2], y[3]), false,
+                                                                         false);
+                        // lane group g now holds sub-tile fn + (g & 1), columns 8*(g >> 1) .. +7
+                        const int col = wcol0 + (fn + (lgrp & 1)) * MF + (lgrp >> 1) * 8;
+                        if (row_ok && col < p.n) *(uint4*)(drow + col) = uint4{s0[0], s1[0], s0[1], s1[1]};
+                    }
+                    if constexpr (FN % 2 == 1) {
+                        const vacc& x = acc[fm][FN - 1];
+                        const int col = wcol0 + (FN - 1) * MF + lgrp * 4;
+                        if (row_ok && col < p.n) *(uint2*)(drow + col) = uint2{pack2(x[0], x[1]), pack2(x[2], x[3])};
+                    }
+                } else {
 #pragma unroll
-                    for (int q = 0; q < NACC / 4; ++q) {
-                        const int col = wcol0 + fn * MF + q * 8 + lgrp * 4;
-                        if (col < p.n) {
-                            v4bf o;
-                            o.x = (__bf16)acc[fm][fn][4 * q + 0];
-                            o.y = (__bf16)acc[fm][fn][4 * q + 1];
-                            o.z = (__bf16)acc[fm][fn][4 * q + 2];
-                            o.w = (__bf16)acc[fm][fn][4 * q + 3];
-                            *(v4bf*)(drow + col) = o;
+                    for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+                        for (int q = 0; q < NACC / 4; ++q) {
+                            const int col = wcol0 + fn * MF + q * 8 + lgrp * 4;
+                            if (row_ok && col < p.n)
+                                *(uint2*)(drow + col) = uint2{pack2(acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1]),
+                                                              pack2(acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3])};
                         }
                     }
                 }
