@@ -51,6 +51,7 @@ typedef __attribute__((address_space(3))) const float lds_f32;
 constexpr int kKBlock = 128;        // K bytes per scale block == K of one MFMA
 constexpr int kMaxMaskedGroups = 1024;
 constexpr int kXcds = 8;
+constexpr int kMAlign = 128;        // contiguous layout: rows per segment block (alignment)
 
 // 16-byte chunk swizzle of a 128-byte LDS row.  Depends on row bits 0..3 only,
 // so it is a per-lane constant for fragment reads (rows 16q + lane%16); it makes
@@ -92,6 +93,15 @@ __device__ __forceinline__ void wait_vmem_le() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// f(integral_constant<I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
 __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -125,11 +135,15 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
 
     // NST stage buffers, each its own array so the compiler can prove that fragment
     // reads of one stage never alias the copies in flight into another.
-    static_assert(NST >= 2 && NST <= 4, "2..4 LDS stages");
+    static_assert(NST >= 2 && NST <= 8, "2..8 LDS stages");
     __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t smem2[NST > 2 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t smem3[NST > 3 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem4[NST > 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem5[NST > 5 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem6[NST > 6 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem7[NST > 7 ? STAGE : 16];
     __shared__ int s_prefix[LAYOUT == kMasked ? kMaxMaskedGroups + 1 : 1];
 
     const int tid = threadIdx.x;
@@ -214,13 +228,49 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             mb = first_m + r % gm;
             nb = r / gm;
             valid_rows = p.rows - mb * BM;
-            if constexpr (LAYOUT == kContiguous) {
-                g = p.m_indices[mb * BM];
-                if (g < 0 || g >= p.num_groups) continue;   // padding block / no such group
-            }
         }
         valid_rows = valid_rows > BM ? BM : valid_rows;
         const int m0 = mb * BM, n0 = nb * BN;
+
+        // Contiguous layout: the group of every 128-row segment block is the index of
+        // its first row (-1 or out of range: padding, skipped).  A tile of two segment
+        // blocks that belong to different groups is computed in two passes, one per
+        // group, each keeping only its own rows.
+        int npass = 1, pg[2] = {g, g}, plo[2] = {0, 0}, phi[2] = {BM, BM};
+        if constexpr (LAYOUT == kContiguous) {
+            auto group_at = [&](int r) {
+                if (r >= valid_rows) return -1;
+                const int v = p.m_indices[m0 + r];
+                return (v < 0 || v >= p.num_groups) ? -1 : v;
+            };
+            if constexpr (BM > kMAlign) {
+                static_assert(BM == 2 * kMAlign, "at most two segment blocks per tile");
+                const int g0 = group_at(0), g1 = group_at(kMAlign);
+                if (g0 < 0 && g1 < 0) continue;
+                if (g0 >= 0 && g1 == g0) {
+                    pg[0] = g0;
+                } else if (g0 >= 0 && g1 < 0) {
+                    pg[0] = g0;
+                    phi[0] = kMAlign;
+                } else if (g0 < 0) {
+                    pg[0] = g1;
+                    plo[0] = kMAlign;
+                } else {
+                    npass = 2;
+                    pg[0] = g0;
+                    phi[0] = kMAlign;
+                    pg[1] = g1;
+                    plo[1] = kMAlign;
+                }
+            } else {
+                pg[0] = group_at(0);
+                if (pg[0] < 0) continue;
+            }
+        }
+        for (int pass = 0; pass < npass; ++pass) {
+        g = pass == 0 ? pg[0] : pg[1];
+        const int row_lo = pass == 0 ? plo[0] : plo[1];
+        const int row_hi = pass == 0 ? phi[0] : phi[1];
 
         const int a_last = p.rows - 1 - m0;   // last readable row, relative to the tile
         const int b_last = p.n - 1 - n0;
@@ -304,7 +354,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 sb_off[fn] = min((wcol0 + fn * MF) / kKBlock, p.nblocks - 1) * KB * 4;
         }
         const __amdgpu_buffer_rsrc_t rs_sa = make_rsrc(sa_tile, ((long)KB * p.ld_sa - m0) * 4);
-        const bool wave_active = wm * WTM < valid_rows;
+        const bool wave_active = wm * WTM < min(valid_rows, row_hi) && wm * WTM + WTM > row_lo;
 
         vacc acc[FM][FN];
 #pragma unroll
@@ -392,7 +442,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         static_assert(kLag <= JB, "the previous block's scales are dead by the barrier");
 
         Scales sc[NST];
-        uint8_t* const stage_buf[4] = {smem0, smem1, smem2, smem3};
+        uint8_t* const stage_buf[8] = {smem0, smem1, smem2, smem3, smem4, smem5, smem6, smem7};
         constexpr int NH = MF == 32 ? 2 : 1;
         v8i af[FM][NH], bf[NH], bnext;
         vacc part[R];
@@ -564,26 +614,15 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             // loop has a single exit, which keeps the register allocator from
             // splitting the accumulators' live ranges around mid-body exits
             const int KF = KB - KB % NST;
-            for (int kb = 0; kb < KF; kb += NST) {
-                block(std::integral_constant<int, 0>{}, kb);
-                block(std::integral_constant<int, 1>{}, kb + 1);
-                if constexpr (NST > 2) block(std::integral_constant<int, 2 % NST>{}, kb + 2);
-                if constexpr (NST > 3) block(std::integral_constant<int, 3 % NST>{}, kb + 3);
-            }
-            if constexpr (NST > 1) {
-                if (KF < KB) block(std::integral_constant<int, 0>{}, KF);
-            }
-            if constexpr (NST > 2) {
-                if (KF + 1 < KB) block(std::integral_constant<int, 1>{}, KF + 1);
-            }
-            if constexpr (NST > 3) {
-                if (KF + 2 < KB) block(std::integral_constant<int, 2 % NST>{}, KF + 2);
-            }
+            for (int kb = 0; kb < KF; kb += NST)
+                static_for<0, NST>([&](auto u) { block(u, kb + decltype(u)::value); });
+            static_for<0, NST - 1>([&](auto u) {
+                if (KF + decltype(u)::value < KB) block(u, KF + decltype(u)::value);
+            });
             const int ul = (KB - 1) % NST;
-            if (ul == 0) drain(std::integral_constant<int, 0>{});
-            if (ul == 1) drain(std::integral_constant<int, 1>{});
-            if constexpr (NST > 2) if (ul == 2) drain(std::integral_constant<int, 2 % NST>{});
-            if constexpr (NST > 3) if (ul == 3) drain(std::integral_constant<int, 3 % NST>{});
+            static_for<0, NST>([&](auto u) {
+                if (ul == decltype(u)::value) drain(u);
+            });
         } else {
             // a wave with no valid rows (masked / short tiles) still copies its share
             // of every stage (operands and A scales) and meets every barrier
@@ -615,7 +654,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
                 const int lr = wm * WTM + fm * MF + lsub;     // row inside the tile
-                bool row_ok = lr < valid_rows;
+                bool row_ok = lr >= row_lo && lr < row_hi && lr < valid_rows;
                 if constexpr (LAYOUT == kContiguous) {
                     if (row_ok) row_ok = p.m_indices[m0 + lr] >= 0;
                 }
@@ -657,6 +696,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         // tile (or another workgroup) reuses these buffers; then every wave is done
         wait_vmem_le<0>();
         __syncthreads();
+        }   // pass
     }
 }
 
@@ -688,6 +728,7 @@ static const KernelConfig kConfigs[] = {
     DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00),
     DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55),
     DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95),
+    DG_CFG(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30),
     // masked
     DG_CFG(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00),
     DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00),
