@@ -734,6 +734,7 @@ static const KernelConfig kConfigs[] = {
     DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00),
     DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90),
     DG_CFG(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90),
+    DG_CFG(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10),
 };
 
 const KernelConfig* kernel_configs(int* count) {
