@@ -64,6 +64,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
 }
 
+// One 16-byte-per-lane copy from a buffer straight into LDS (a named device
+// function, so that only the device compilation ever checks the 16-byte form).
+__device__ __forceinline__ void buffer_copy_lds16(__amdgpu_buffer_rsrc_t rs, lds_void* dst, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 0);
+}
+
 // One fp32 from a buffer (per-lane byte offset + scalar byte offset).
 __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
@@ -112,7 +118,7 @@ __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC0
 // The 32x32 form needs one scale product per 16 promotion FMAs instead of per 4,
 // and its 32-column sub-tiles never straddle a 128-column scale block when the
 // tile offsets are multiples of 32.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE>
 __global__ void __launch_bounds__(WM * WN * 64)
 dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const float* __restrict__ sa_ptr,
                const uint8_t* __restrict__ b_ptr, const float* __restrict__ sb_ptr, uint16_t* __restrict__ d_ptr) {
@@ -192,450 +198,553 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
 
     const int P = gridDim.x;
     const int w = blockIdx.x;
-    for (int step = 0;; ++step) {
-        // ---- tile index: XCD-aware hand-out of the linear tile order ----
-        int L;
-        if (p.xcd_remap) L = step * P + (w % kXcds) * (P / kXcds) + (w / kXcds);
-        else L = step * P + w;
-        if (step * P >= total_tiles) break;
-        if (L >= total_tiles) continue;   // uniform; this workgroup idles this step
+    constexpr int NSLOT = A_PER + B_PER;
 
-        int g = 0, mb, nb, valid_rows;
-        if constexpr (LAYOUT == kMasked) {
-            // group g owns tiles [prefix[g], prefix[g+1]) * tiles_n, ordered N block
-            // major and row block minor, so the row blocks sharing one B tile are
-            // neighbours in the hand-out (same XCD, same step: B comes from L2 once)
-            const int q = L / p.tiles_n;
-            int lo = 0, hi = p.num_groups;           // largest g with prefix[g] <= q
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (s_prefix[mid] <= q) lo = mid; else hi = mid;
-            }
-            g = lo;
-            const int vb = s_prefix[g + 1] - s_prefix[g];
-            const int t = L - s_prefix[g] * p.tiles_n;
-            nb = t / vb;
-            mb = t - nb * vb;
-            int mm = p.masked_m[g];
-            mm = mm < 0 ? 0 : (mm > p.rows ? p.rows : mm);
-            valid_rows = mm - mb * BM;
-        } else {
-            const int gsz = p.group_m * p.tiles_n;
-            const int grp = L / gsz;
-            const int first_m = grp * p.group_m;
-            const int gm = min(p.tiles_m - first_m, p.group_m);
-            const int r = L - grp * gsz;
-            mb = first_m + r % gm;
-            nb = r / gm;
-            valid_rows = p.rows - mb * BM;
-        }
-        valid_rows = valid_rows > BM ? BM : valid_rows;
-        const int m0 = mb * BM, n0 = nb * BN;
+    // ---- operand copies: 8-row slots dealt round robin to the waves.  Each lane's
+    // 32-bit source offset inside a tile is the same for every tile and K block;
+    // rows past an operand's end fall outside the tile's buffer descriptor, so their
+    // copies read nothing and write zeros (their outputs are never stored). ----
+    uint32_t a_off[A_PER], b_off[B_PER];
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+        const int srow = min(wave + i * NW, A_SLOTS - 1) * 8 + (lane >> 3);
+        a_off[i] = (uint32_t)srow * (uint32_t)p.lda + (uint32_t)((((lane & 7) ^ swz(srow))) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) {
+        const int srow = min(wave + i * NW, B_SLOTS - 1) * 8 + (lane >> 3);
+        b_off[i] = (uint32_t)srow * (uint32_t)p.ldb + (uint32_t)((((lane & 7) ^ swz(BM + srow))) * 16);
+    }
+    // A scales: a wave's rows of a K block are contiguous in sA (MN-major), so they
+    // travel to LDS with the block's operands, one 4-byte copy per lane (row
+    // wm*WTM + lane) into the wave's own 256-byte area of the stage.  The K offset
+    // is in the per-lane offset, which the descriptor bounds (rows past the end of
+    // sA read zeros).
+    const uint32_t sa_voff = (uint32_t)(wm * WTM + lane) * 4u;
+    const int sa_lds = ROWS * kKBlock + wave * 256 + lsub * 4;   // this lane's row, sub-tile 0
+    constexpr int NSB = MF == 16 ? 2 : FN;
 
-        // Contiguous layout: the group of every 128-row segment block is the index of
-        // its first row (-1 or out of range: padding, skipped).  A tile of two segment
-        // blocks that belong to different groups is computed in two passes, one per
-        // group, each keeping only its own rows.
-        int npass = 1, pg[2] = {g, g}, plo[2] = {0, 0}, phi[2] = {BM, BM};
-        if constexpr (LAYOUT == kContiguous) {
-            auto group_at = [&](int r) {
-                if (r >= valid_rows) return -1;
-                const int v = p.m_indices[m0 + r];
-                return (v < 0 || v >= p.num_groups) ? -1 : v;
-            };
-            if constexpr (BM > kMAlign) {
-                static_assert(BM == 2 * kMAlign, "at most two segment blocks per tile");
-                const int g0 = group_at(0), g1 = group_at(kMAlign);
-                if (g0 < 0 && g1 < 0) continue;
-                if (g0 >= 0 && g1 == g0) {
-                    pg[0] = g0;
-                } else if (g0 >= 0 && g1 < 0) {
-                    pg[0] = g0;
-                    phi[0] = kMAlign;
-                } else if (g0 < 0) {
-                    pg[0] = g1;
-                    plo[0] = kMAlign;
-                } else {
-                    npass = 2;
-                    pg[0] = g0;
-                    phi[0] = kMAlign;
-                    pg[1] = g1;
-                    plo[1] = kMAlign;
+    // ---- one tile (or one pass of a two-group contiguous tile): everything its
+    // copies, scales and epilogue need, all wave-uniform ----
+    // (rows [row_lo, row_hi) of the tile are this pass's valid rows)
+    struct Tile {
+        int m0, row_lo, row_hi, wcol0;
+        unsigned hi_mask;
+        int sb_off[NSB];
+        bool active;
+        __amdgpu_buffer_rsrc_t rs_a, rs_b, rs_sa;
+        const float* sb_grp;
+        uint16_t* d_tile;
+    };
+    // the tile hand-out: step s gives workgroup w the tile L(s, w); a contiguous
+    // tile holding two groups yields two passes
+    int step = 0, pass = 0, npass = 0, st_m0 = 0, st_n0 = 0, st_vr = 0;
+    int pg[2] = {0, 0}, plo[2] = {0, 0}, phi[2] = {BM, BM};
+    auto fetch_step = [&]() -> bool {   // from `step` on, the first step with work
+        for (;; ++step) {
+            if (step * P >= total_tiles) return false;
+            // ---- tile index: XCD-aware hand-out of the linear tile order ----
+            int L;
+            if (p.xcd_remap) L = step * P + (w % kXcds) * (P / kXcds) + (w / kXcds);
+            else L = step * P + w;
+            if (L >= total_tiles) continue;   // uniform; this workgroup idles this step
+            int g = 0, mb, nb, valid_rows;
+            if constexpr (LAYOUT == kMasked) {
+                // group g owns tiles [prefix[g], prefix[g+1]) * tiles_n, ordered N block
+                // major and row block minor, so the row blocks sharing one B tile are
+                // neighbours in the hand-out (same XCD, same step: B comes from L2 once)
+                const int q = L / p.tiles_n;
+                int lo = 0, hi = p.num_groups;           // largest g with prefix[g] <= q
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_prefix[mid] <= q) lo = mid; else hi = mid;
                 }
+                g = lo;
+                const int vb = s_prefix[g + 1] - s_prefix[g];
+                const int t = L - s_prefix[g] * p.tiles_n;
+                nb = t / vb;
+                mb = t - nb * vb;
+                int mm = p.masked_m[g];
+                mm = mm < 0 ? 0 : (mm > p.rows ? p.rows : mm);
+                valid_rows = mm - mb * BM;
             } else {
-                pg[0] = group_at(0);
-                if (pg[0] < 0) continue;
+                const int gsz = p.group_m * p.tiles_n;
+                const int grp = L / gsz;
+                const int first_m = grp * p.group_m;
+                const int gm = min(p.tiles_m - first_m, p.group_m);
+                const int r = L - grp * gsz;
+                mb = first_m + r % gm;
+                nb = r / gm;
+                valid_rows = p.rows - mb * BM;
             }
+            valid_rows = valid_rows > BM ? BM : valid_rows;
+            st_m0 = mb * BM;
+            st_n0 = nb * BN;
+            st_vr = valid_rows;
+            npass = 1;
+            pg[0] = pg[1] = g;
+            plo[0] = plo[1] = 0;
+            phi[0] = phi[1] = BM;
+            // Contiguous layout: the group of every 128-row segment block is the index
+            // of its first row (-1 or out of range: padding, skipped).  A tile of two
+            // segment blocks that belong to different groups is computed in two passes,
+            // one per group, each keeping only its own rows.
+            if constexpr (LAYOUT == kContiguous) {
+                auto group_at = [&](int r) {
+                    if (r >= valid_rows) return -1;
+                    const int v = p.m_indices[st_m0 + r];
+                    return (v < 0 || v >= p.num_groups) ? -1 : v;
+                };
+                if constexpr (BM > kMAlign) {
+                    static_assert(BM == 2 * kMAlign, "at most two segment blocks per tile");
+                    const int g0 = group_at(0), g1 = group_at(kMAlign);
+                    if (g0 < 0 && g1 < 0) continue;
+                    if (g0 >= 0 && g1 == g0) {
+                        pg[0] = g0;
+                    } else if (g0 >= 0 && g1 < 0) {
+                        pg[0] = g0;
+                        phi[0] = kMAlign;
+                    } else if (g0 < 0) {
+                        pg[0] = g1;
+                        plo[0] = kMAlign;
+                    } else {
+                        npass = 2;
+                        pg[0] = g0;
+                        phi[0] = kMAlign;
+                        pg[1] = g1;
+                        plo[1] = kMAlign;
+                    }
+                } else {
+                    pg[0] = group_at(0);
+                    if (pg[0] < 0) continue;
+                }
+            }
+            return true;
         }
-        for (int pass = 0; pass < npass; ++pass) {
-        g = pass == 0 ? pg[0] : pg[1];
-        const int row_lo = pass == 0 ? plo[0] : plo[1];
-        const int row_hi = pass == 0 ? phi[0] : phi[1];
-
-        const int a_last = p.rows - 1 - m0;   // last readable row, relative to the tile
-        const int b_last = p.n - 1 - n0;
+    };
+    // the tile the hand-out state describes
+    auto build_tile = [&](Tile& t) {
+        const int g = pass == 0 ? pg[0] : pg[1];
+        const int m0 = st_m0, n0 = st_n0, valid_rows = st_vr;
+        t.m0 = m0;
+        t.row_lo = pass == 0 ? plo[0] : plo[1];
+        t.row_hi = min(pass == 0 ? phi[0] : phi[1], valid_rows);
         const uint8_t* a_tile = a_ptr + (LAYOUT == kMasked ? (long)g * p.a_gstride : 0) + (long)m0 * p.lda;
         const uint8_t* b_tile = b_ptr + (long)g * p.b_gstride + (long)n0 * p.ldb;
         const float* sa_tile = sa_ptr + (LAYOUT == kMasked ? (long)g * p.sa_gstride : 0) + m0;
-        const float* sb_grp = sb_ptr + (long)g * p.sb_gstride;
-        uint16_t* d_base = d_ptr + (LAYOUT == kMasked ? (long)g * p.d_gstride : 0);
-
-        // ---- operand copies: 8-row slots dealt round robin to the waves; each lane's
-        // 32-bit source offset inside the tile is fixed for the whole K loop (tails
-        // are clamped to the last real row) ----
-        uint32_t a_off[A_PER], b_off[B_PER];
-#pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
-            const int srow = min(wave + i * NW, A_SLOTS - 1) * 8 + (lane >> 3);
-            const int r = srow > a_last ? a_last : srow;
-            a_off[i] = (uint32_t)r * (uint32_t)p.lda + (uint32_t)((((lane & 7) ^ swz(srow))) * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            const int srow = min(wave + i * NW, B_SLOTS - 1) * 8 + (lane >> 3);
-            const int r = srow > b_last ? b_last : srow;
-            b_off[i] = (uint32_t)r * (uint32_t)p.ldb + (uint32_t)((((lane & 7) ^ swz(BM + srow))) * 16);
-        }
+        t.sb_grp = sb_ptr + (long)g * p.sb_gstride;
+        t.d_tile = d_ptr + (LAYOUT == kMasked ? (long)g * p.d_gstride : 0) + (long)m0 * p.ldd;
         // Buffer descriptors over this tile's operands: the K offset of each stage
         // travels in a scalar register, so issuing a stage costs no vector ALU work.
         // Masked layout: rows at or past masked_m fall outside the descriptor, so their
         // copies return zeros without a memory access (their outputs are never stored).
-        const int a_rows_read = LAYOUT == kMasked ? valid_rows : a_last + 1;
-        const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a_tile, (long)a_rows_read * p.lda);
-        const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b_tile, (long)(b_last + 1) * p.ldb);
-        // DMA slot t of this wave (A slots first, then B slots) for K block kb.  A slot
-        // index past the last one repeats the last slot: the same bytes land on the
-        // same LDS location twice, which keeps the issue free of branches.
-        constexpr int NSLOT = A_PER + B_PER;
-        auto issue_slot = [&](uint8_t* smem, int kb, int t) {
-            const int koff = kb * kKBlock;
-            if (t < A_PER) {
-                const int j = min(wave + t * NW, A_SLOTS - 1);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void*)(smem + j * 1024), 16,
-                                                         (int)a_off[t], koff, 0, 0);
-            } else {
-                const int j = min(wave + (t - A_PER) * NW, B_SLOTS - 1);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(smem + BM * kKBlock + j * 1024), 16,
-                                                         (int)b_off[t - A_PER], koff, 0, 0);
-            }
-        };
-        auto issue_stage = [&](uint8_t* smem, int kb) {
-#pragma unroll
-            for (int t = 0; t < NSLOT; ++t) issue_slot(smem, kb, t);
-        };
-
-        // ---- scale sources ----
-        // A scales: a wave's rows of a K block are contiguous in sA (MN-major), so they
-        // travel to LDS with the block's operands, one 4-byte copy per lane (row
-        // wm*WTM + lane) into the wave's own 256-byte area of the stage.  The K offset
-        // is in the per-lane offset, which the descriptor bounds (rows past the end of
-        // sA read zeros).
-        const uint32_t sa_voff = (uint32_t)(wm * WTM + lane) * 4u;
-        const int sa_lds = ROWS * kKBlock + wave * 256 + lsub * 4;   // this lane's row, sub-tile 0
+        const int a_rows_read = LAYOUT == kMasked ? valid_rows : p.rows - m0;
+        t.rs_a = make_rsrc(a_tile, (long)a_rows_read * p.lda);
+        t.rs_b = make_rsrc(b_tile, (long)(p.n - n0) * p.ldb);
+        t.rs_sa = make_rsrc(sa_tile, ((long)KB * p.ld_sa - m0) * 4);
         // Sub-tile column fn (MF columns, inside one 128-column scale block because MF
         // divides 128 and the column offsets are multiples of MF) reads its B scales
         // from row nb(fn) of sB; the byte offset of that row is wave-uniform.
         // With MF=16 a wave spans at most 128 columns, i.e. two scale rows (lo, hi):
         // two loads per K block and a per-column choice by a uniform bit mask.
-        const int wcol0 = n0 + wn * WTN;
-        constexpr int NSB = MF == 16 ? 2 : FN;
-        int sb_off[NSB];
-        unsigned hi_mask = 0;
+        t.wcol0 = n0 + wn * WTN;
+        t.hi_mask = 0;
         if constexpr (MF == 16) {
-            const int nb_lo = min(wcol0 / kKBlock, p.nblocks - 1);
-            sb_off[0] = nb_lo * KB * 4;
-            sb_off[1] = min(nb_lo + 1, p.nblocks - 1) * KB * 4;
+            const int nb_lo = min(t.wcol0 / kKBlock, p.nblocks - 1);
+            t.sb_off[0] = nb_lo * KB * 4;
+            t.sb_off[1] = min(nb_lo + 1, p.nblocks - 1) * KB * 4;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                if ((wcol0 + fn * MF) / kKBlock > nb_lo) hi_mask |= 1u << fn;
+                if ((t.wcol0 + fn * MF) / kKBlock > nb_lo) t.hi_mask |= 1u << fn;
         } else {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                sb_off[fn] = min((wcol0 + fn * MF) / kKBlock, p.nblocks - 1) * KB * 4;
+                t.sb_off[fn] = min((t.wcol0 + fn * MF) / kKBlock, p.nblocks - 1) * KB * 4;
         }
-        const __amdgpu_buffer_rsrc_t rs_sa = make_rsrc(sa_tile, ((long)KB * p.ld_sa - m0) * 4);
-        const bool wave_active = wm * WTM < min(valid_rows, row_hi) && wm * WTM + WTM > row_lo;
+        t.active = wm * WTM < t.row_hi && wm * WTM + WTM > t.row_lo;
+    };
+    // no tile: its copies read nothing (every lane is out of range) and write zeros
+    auto null_tile = [&](Tile& t) {
+        t.m0 = t.row_lo = t.row_hi = t.wcol0 = 0;
+        t.hi_mask = 0;
+#pragma unroll
+        for (int i = 0; i < NSB; ++i) t.sb_off[i] = 0;
+        t.active = false;
+        t.rs_a = t.rs_b = t.rs_sa = make_rsrc(a_ptr, 0);
+        t.sb_grp = sb_ptr;
+        t.d_tile = d_ptr;
+    };
+    // move the hand-out state to the tile after the current one; false when none is left
+    auto advance = [&]() -> bool {
+        if (pass + 1 < npass) {
+            ++pass;
+            return true;
+        }
+        ++step;
+        pass = 0;
+        return fetch_step();
+    };
 
-        vacc acc[FM][FN];
+    Tile cur, nx;
+    if (!fetch_step()) return;   // uniform: no work for this workgroup
+    build_tile(cur);
+
+    // DMA slot t of this wave (A slots first, then B slots) for K block kb of tile
+    // tl.  A slot index past the last one repeats the last slot: the same bytes land
+    // on the same LDS location twice, which keeps the issue free of branches.
+    auto issue_slot = [&](const Tile& tl, uint8_t* smem, int kb, int t) {
+        const int koff = kb * kKBlock;
+        if (t < A_PER) {
+            const int j = min(wave + t * NW, A_SLOTS - 1);
+            buffer_copy_lds16(tl.rs_a, (lds_void*)(smem + j * 1024), (int)a_off[t], koff);
+        } else {
+            const int j = min(wave + (t - A_PER) * NW, B_SLOTS - 1);
+            buffer_copy_lds16(tl.rs_b, (lds_void*)(smem + BM * kKBlock + j * 1024), (int)b_off[t - A_PER], koff);
+        }
+    };
+    auto issue_sa = [&](const Tile& tl, uint8_t* smem, int kb) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(tl.rs_sa,
+                                                 (lds_void*)(smem + ROWS * kKBlock + wave * 256), 4,
+                                                 (int)(sa_voff + (uint32_t)(kb * p.ld_sa) * 4u), 0, 0, 0);
+    };
+    auto issue_stage = [&](const Tile& tl, uint8_t* smem, int kb) {
+#pragma unroll
+        for (int t = 0; t < NSLOT; ++t) issue_slot(tl, smem, kb, t);
+        issue_sa(tl, smem, kb);
+    };
+
+    // per-lane LDS byte offsets of the 16-byte chunks of this lane's fragment
+    // (MF=16: chunks 2g, 2g+1 of the 128-K row; MF=32: chunks 4h+2g, 4h+2g+1 for
+    // K half h), swizzled like the rows were written
+    int coff[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            coff[h][e] = (((MF == 16 ? 2 * lgrp : 4 * h + 2 * lgrp) + e) ^ swz(lane & 15)) * 16;
+
+    // Scales of one K block: a[fm] per lane (its row of sub-tile row fm), b[t]
+    // wave-uniform (scalar loads of sB, which never pass through the texture unit)
+    struct Scales { float a[FM]; float b[NSB]; };
+    auto load_sb = [&](const Tile& tl, Scales& sc, int kb) {
+#pragma unroll
+        for (int t = 0; t < NSB; ++t) sc.b[t] = tl.sb_grp[(tl.sb_off[t] >> 2) + kb];
+    };
+    auto read_sa = [&](Scales& sc, const uint8_t* smem) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = vacc{};
+            sc.a[fm] = *(const lds_f32*)((const lds_u8*)smem + sa_lds + fm * MF * 4);
+    };
+    // the B scale of sub-tile column fn as a scalar: MF=16 picks the wave's low or
+    // high scale row with uniform integer operations
+    auto pick_b = [&](const Scales& sc, int fn) -> float {
+        if constexpr (MF == 16) {
+            const unsigned m = 0u - ((cur.hi_mask >> fn) & 1u);
+            const unsigned lo = __builtin_bit_cast(unsigned, sc.b[0]);
+            const unsigned hi = __builtin_bit_cast(unsigned, sc.b[NSB - 1]);
+            return __builtin_bit_cast(float, lo ^ ((lo ^ hi) & m));
+        } else {
+            return sc.b[fn];
+        }
+    };
 
-        // per-lane LDS byte offsets of the 16-byte chunks of this lane's fragment
-        // (MF=16: chunks 2g, 2g+1 of the 128-K row; MF=32: chunks 4h+2g, 4h+2g+1 for
-        // K half h), swizzled like the rows were written
-        int coff[2][2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                coff[h][e] = (((MF == 16 ? 2 * lgrp : 4 * h + 2 * lgrp) + e) ^ swz(lane & 15)) * 16;
+    // ---- K loop: one continuous stream of steps over (K block, column fn, row fm).
+    // Step j of a block issues the MFMA(s) of sub-tile (fm, fn) = (j % FM, j / FM)
+    // and promotes the partial of the step kLag earlier, which may belong to the
+    // previous K block (its scales are still held), so the matrix core never
+    // waits for a promotion and a block boundary costs no pipeline drain.
+    // LDS stages: block kb lives in stage kb % NST.  In each block the single
+    // workgroup barrier follows the first MFMA of the last column (step JB).  By
+    // then every wave has finished reading this block's stage, except for the
+    // fragments already in registers, and has waited for its own copies of the
+    // next block, so after the barrier
+    //   * the next block's fragments are read while the last column's MFMAs run
+    //     (each A fragment as soon as its last MFMA of this block is issued), and
+    //   * the stage read in this block is free: the copies of block kb + NST go
+    //     there, issued every other step and running on into the next block.
+    // When K/128 is a multiple of NST, the blocks past the last one are the next
+    // tile's first blocks: their copies, A scales and fragments arrive while this
+    // tile finishes, so a tile boundary costs no pipeline refill either.
+    constexpr int NJ = FN * FM;
+    constexpr int JB = (FN - 1) * FM;
+    static_assert(FN >= 2, "the barrier sits in the last of at least two columns");
+    // ring of in-flight partials: its position is a compile-time function of the
+    // step because the block loop is unrolled by NST
+    constexpr int R = MF == 32 ? 2
+                    : ((NST * NJ) % 4 == 0 ? 4 : ((NST * NJ) % 3 == 0 ? 3 : 2));
+    static_assert((NST * NJ) % R == 0, "partial ring must tile the unrolled loop");
+    constexpr int kLag = R - 1;
+    constexpr int NVM = NSLOT + 1;             // vector memory instructions per block
+    // Copies of block kb + NST (NSLOT operand slots, then the A-scale copy) go to
+    // stage kb % NST as soon as block kb's barrier has freed it: copy t at step
+    // JB + 1 + t*CPN/CPD of block kb (two steps apart when a block is long enough),
+    // running on into the first steps of block kb+1, never past its barrier
+    // (where, for NST=2, they must have landed).
+    constexpr int NDMA = NSLOT + 1;
+    constexpr int CPN = 2 * NDMA + 4 <= NJ ? 2 : (NDMA + 4 <= NJ ? 1 : NJ);
+    constexpr int CPD = CPN == NJ ? NDMA : 1;
+    static_assert((NDMA - 1) * CPN / CPD + 1 <= NJ, "copies must be issued before the next barrier");
+    constexpr int NFIRST = [] {   // copies issued in the freeing block
+        int c = 0;
+        for (int t = 0; t < NDMA; ++t) c += JB + 1 + t * CPN / CPD < NJ;
+        return c;
+    }();
+    static_assert(kLag <= JB, "the previous block's scales are dead by the barrier");
+    // copy t of block kb of tile tl into stage smem (blocks past the last one of a
+    // tile that is not followed by pipelined work re-read block KB-1)
+    auto issue_copy = [&](const Tile& tl, int t, uint8_t* smem, int kb) {
+        if (t < NSLOT) issue_slot(tl, smem, kb, t);
+        else issue_sa(tl, smem, kb);
+    };
 
-        // Scales of one K block: a[fm] per lane (its row of sub-tile row fm), b[t]
-        // wave-uniform (scalar loads of sB, which never pass through the texture unit)
-        struct Scales { float a[FM]; float b[NSB]; };
-        auto issue_sa = [&](uint8_t* smem, int kb) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_sa, (lds_void*)(smem + ROWS * kKBlock + wave * 256), 4,
-                                                     (int)(sa_voff + (uint32_t)(kb * p.ld_sa) * 4u), 0, 0, 0);
-        };
-        auto load_sb = [&](Scales& sc, int kb) {
+    Scales sc[NST];
+    uint8_t* const stage_buf[8] = {smem0, smem1, smem2, smem3, smem4, smem5, smem6, smem7};
+    constexpr int NH = MF == 32 ? 2 : 1;
+    v8i af[FM][NH], bf[NH], bnext;
+    vacc part[R];
+    vacc acc[FM][FN];
+    const int arow0 = wm * WTM, bcol0 = BM + wn * WTN;
+
+    // This lane's byte offsets in a stage, made opaque to the compiler so that
+    // every fragment read is stage + offset + an immediate row offset instead
+    // of a separately hoisted address register per fragment and stage.  Only
+    // the offset is hidden: the stage array stays visible, so the compiler
+    // knows which stage a read touches and that it is not one the copies fill.
+    auto lane_base = [&](const uint8_t* smem, lds_u8* (&lb)[2][2]) {
 #pragma unroll
-            for (int t = 0; t < NSB; ++t) sc.b[t] = sb_grp[(sb_off[t] >> 2) + kb];
-        };
-        auto read_sa = [&](Scales& sc, const uint8_t* smem) {
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-                sc.a[fm] = *(const lds_f32*)((const lds_u8*)smem + sa_lds + fm * MF * 4);
-        };
-        // the B scale of sub-tile column fn as a scalar: MF=16 picks the wave's low or
-        // high scale row with uniform integer operations
-        auto pick_b = [&](const Scales& sc, int fn) -> float {
-            if constexpr (MF == 16) {
-                const unsigned m = 0u - ((hi_mask >> fn) & 1u);
-                const unsigned lo = __builtin_bit_cast(unsigned, sc.b[0]);
-                const unsigned hi = __builtin_bit_cast(unsigned, sc.b[NSB - 1]);
-                return __builtin_bit_cast(float, lo ^ ((lo ^ hi) & m));
-            } else {
-                return sc.b[fn];
+            for (int e = 0; e < 2; ++e) {
+                int off = lsub * kKBlock + coff[h][e];
+                asm volatile("" : "+v"(off));
+                lb[h][e] = (lds_u8*)smem + off;
             }
-        };
-
-        // ---- K loop: one continuous stream of steps over (K block, column fn, row fm).
-        // Step j of a block issues the MFMA(s) of sub-tile (fm, fn) = (j % FM, j / FM)
-        // and promotes the partial of the step kLag earlier, which may belong to the
-        // previous K block (its scales are still held), so the matrix core never
-        // waits for a promotion and a block boundary costs no pipeline drain.
-        // LDS stages: block kb lives in stage kb % NST.  In each block the single
-        // workgroup barrier follows the first MFMA of the last column (step JB).  By
-        // then every wave has finished reading this block's stage, except for the
-        // fragments already in registers, and has waited for its own copies of the
-        // next block, so after the barrier
-        //   * the next block's fragments are read while the last column's MFMAs run
-        //     (each A fragment as soon as its last MFMA of this block is issued), and
-        //   * the stage read in the previous block is free: the copies of block
-        //     kb + NST - 1 go there, issued one per step early in the next block.
-        constexpr int NJ = FN * FM;
-        constexpr int JB = (FN - 1) * FM;
-        static_assert(FN >= 2, "the barrier sits in the last of at least two columns");
-        // ring of in-flight partials: its position is a compile-time function of the
-        // step because the block loop is unrolled by NST
-        constexpr int R = MF == 32 ? 2
-                        : ((NST * NJ) % 4 == 0 ? 4 : ((NST * NJ) % 3 == 0 ? 3 : 2));
-        static_assert((NST * NJ) % R == 0, "partial ring must tile the unrolled loop");
-        constexpr int kLag = R - 1;
-        constexpr int NVM = NSLOT + 1;             // vector memory instructions per block
-        // Copies of block kb + NST (NSLOT operand slots, then the A-scale copy) go to
-        // stage kb % NST as soon as block kb's barrier has freed it: copy t at step
-        // JB + 1 + t*CPN/CPD of block kb (two steps apart when a block is long enough),
-        // running on into the first steps of block kb+1, never past its barrier
-        // (where, for NST=2, they must have landed).
-        constexpr int NDMA = NSLOT + 1;
-        constexpr int CPN = 2 * NDMA + 4 <= NJ ? 2 : (NDMA + 4 <= NJ ? 1 : NJ);
-        constexpr int CPD = CPN == NJ ? NDMA : 1;
-        static_assert((NDMA - 1) * CPN / CPD + 1 <= NJ, "copies must be issued before the next barrier");
-        constexpr int NFIRST = [] {   // copies issued in the freeing block
-            int c = 0;
-            for (int t = 0; t < NDMA; ++t) c += JB + 1 + t * CPN / CPD < NJ;
-            return c;
-        }();
-        static_assert(kLag <= JB, "the previous block's scales are dead by the barrier");
-
-        Scales sc[NST];
-        uint8_t* const stage_buf[8] = {smem0, smem1, smem2, smem3, smem4, smem5, smem6, smem7};
-        constexpr int NH = MF == 32 ? 2 : 1;
-        v8i af[FM][NH], bf[NH], bnext;
-        vacc part[R];
+    };
+    // fragment of sub-tile rows [row0, row0+MF) for K half h (MF=16: whole block)
+    auto frag = [&](lds_u8* const (&lb)[2][2], int row0, int h) -> v8i {
+        const v4i lo = *(const lds_v4i*)(lb[h][0] + row0 * kKBlock);
+        const v4i hi = *(const lds_v4i*)(lb[h][1] + row0 * kKBlock);
+        return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+    // the first block's fragments and scales of a tile, from stage 0 (read in the
+    // order the loop issues a next block's reads: B fragment, A scales, A fragments)
+    auto first_fragments = [&]() {
+        lds_u8* lb[2][2];
+        lane_base(smem0, lb);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            bf[h] = frag(lb, bcol0, h);
+            if (h == 0) read_sa(sc[0], smem0);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) af[fm][h] = frag(lb, arow0 + fm * MF, h);
+        }
+    };
+    // tile start: the "previous block" of block 0 has zero partials and zero scales
+    auto reset_tile = [&]() {
 #pragma unroll
         for (int r = 0; r < R; ++r) part[r] = vacc{};
-        // the "previous block" of the first block: zero partials times zero scales
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) sc[NST - 1].a[fm] = 0.f;
 #pragma unroll
         for (int t = 0; t < NSB; ++t) sc[NST - 1].b[t] = 0.f;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = vacc{};
+    };
 
-        // This lane's byte offsets in a stage, made opaque to the compiler so that
-        // every fragment read is stage + offset + an immediate row offset instead
-        // of a separately hoisted address register per fragment and stage.  Only
-        // the offset is hidden: the stage array stays visible, so the compiler
-        // knows which stage a read touches and that it is not one the copies fill.
-        auto lane_base = [&](const uint8_t* smem, lds_u8* (&lb)[2][2]) {
+    // ---- prologue of the first tile: copies of blocks 0 .. NST-2 and the early
+    // part of block NST-1's (clamped), then the first block's fragments and scales ----
+    auto prologue = [&](const Tile& tl) {
 #pragma unroll
-            for (int h = 0; h < NH; ++h)
+        for (int s = 0; s < NST - 1; ++s) issue_stage(tl, stage_buf[s], s < KB ? s : KB - 1);
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    int off = lsub * kKBlock + coff[h][e];
-                    asm volatile("" : "+v"(off));
-                    lb[h][e] = (lds_u8*)smem + off;
-                }
-        };
-        // fragment of sub-tile rows [row0, row0+MF) for K half h (MF=16: whole block)
-        auto frag = [&](lds_u8* const (&lb)[2][2], int row0, int h) -> v8i {
-            const v4i lo = *(const lds_v4i*)(lb[h][0] + row0 * kKBlock);
-            const v4i hi = *(const lds_v4i*)(lb[h][1] + row0 * kKBlock);
-            return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        };
-        const int arow0 = wm * WTM, bcol0 = BM + wn * WTN;
-
-        auto issue_copy = [&](int t, uint8_t* smem, int kb) {
-            kb = kb < KB ? kb : KB - 1;
-            if (t < NSLOT) issue_slot(smem, kb, t);
-            else issue_sa(smem, kb);
-        };
-        // ---- prologue: copies of blocks 0 .. NST-2 and the early part of block
-        // NST-1's (all clamped), then the first block's fragments and scales ----
-#pragma unroll
-        for (int s = 0; s < NST - 1; ++s) {
-            const int kk = s < KB ? s : KB - 1;
-            issue_stage(stage_buf[s], kk);
-            issue_sa(stage_buf[s], kk);
-        }
-#pragma unroll
-        for (int t = 0; t < NFIRST; ++t) issue_copy(t, stage_buf[NST - 1], NST - 1);
+        for (int t = 0; t < NFIRST; ++t) issue_copy(tl, t, stage_buf[NST - 1], NST - 1 < KB ? NST - 1 : KB - 1);
         // (the scalar loads complete before the loop, so the loop starts with only LDS
-        // reads in flight, in the order the loop itself issues them: B fragment, A
-        // scales, A fragments)
-        if (wave_active) load_sb(sc[0], 0);
+        // reads in flight)
+        if (tl.active) load_sb(tl, sc[0], 0);
         wait_lds_all();
         wait_vmem_le<(NST - 2) * NVM + NFIRST>();
         stage_barrier();
-        if (wave_active) {
-            lds_u8* lb[2][2];
-            lane_base(smem0, lb);
-#pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                bf[h] = frag(lb, bcol0, h);
-                if (h == 0) read_sa(sc[0], smem0);
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) af[fm][h] = frag(lb, arow0 + fm * MF, h);
-            }
-        }
+        if (tl.active) first_fragments();
+    };
+    prologue(cur);
 
-        // One K block (stage U of the unrolled loop, block index kbu).
-        auto block = [&](auto stage_tag, int kbu) {
-            constexpr int U = decltype(stage_tag)::value;
-            const uint8_t* cur = stage_buf[U];
-            const uint8_t* nxt = stage_buf[(U + 1) % NST];
-            uint8_t* dst = stage_buf[(U + NST - 1) % NST];
-            const Scales& scs = sc[U];
-            const Scales& scp = sc[(U + NST - 1) % NST];   // previous block's
-            Scales& scn = sc[(U + 1) % NST];               // next block's (for NST=2: scp's slot)
-            const int nkb = kbu + 1 < KB ? kbu + 1 : KB - 1;
-            lds_u8* lc[2][2];
-            lds_u8* ln[2][2];
-            lane_base(cur, lc);
-            lane_base(nxt, ln);
-            auto scale = [&](bool prev, int fm, int fn) {
-                const Scales& sc = prev ? scp : scs;
-                return sc.a[fm] * pick_b(sc, fn);
-            };
-            auto promote = [&](int q, int i0, int i1) {
-                // q: step index relative to this block, possibly negative (previous block)
-                const int slot = ((U * NJ + q) % R + R) % R;
-                const int qq = q < 0 ? q + NJ : q;
-                const float s = scale(q < 0, qq % FM, qq / FM);
-                const vacc& pq = part[slot];
+    // One K block (stage U of the unrolled loop, block index kbu).  TAIL: one of the
+    // last NST blocks of a tile whose K/128 is a multiple of NST; its copies past
+    // the last block go to the next tile `nx` (blocks kb - KB; a null tile reads
+    // nothing).  Otherwise copies past the last block re-read block KB-1.
+    auto block = [&](auto stage_tag, auto tail_tag, int kbu) {
+        constexpr int U = decltype(stage_tag)::value;
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        const uint8_t* curs = stage_buf[U];
+        const uint8_t* nxt = stage_buf[(U + 1) % NST];
+        uint8_t* dst = stage_buf[(U + NST - 1) % NST];
+        const Scales& scs = sc[U];
+        const Scales& scp = sc[(U + NST - 1) % NST];   // previous block's
+        Scales& scn = sc[(U + 1) % NST];               // next block's (for NST=2: scp's slot)
+        lds_u8* lc[2][2];
+        lds_u8* ln[2][2];
+        lane_base(curs, lc);
+        lane_base(nxt, ln);
+        auto scale = [&](bool prev, int fm, int fn) {
+            const Scales& sc = prev ? scp : scs;
+            return sc.a[fm] * pick_b(sc, fn);
+        };
+        auto promote = [&](int q, int i0, int i1) {
+            // q: step index relative to this block, possibly negative (previous block)
+            const int slot = ((U * NJ + q) % R + R) % R;
+            const int qq = q < 0 ? q + NJ : q;
+            const float s = scale(q < 0, qq % FM, qq / FM);
+            const vacc& pq = part[slot];
 #pragma unroll
-                for (int i = i0; i < i1; ++i)
-                    acc[qq % FM][qq / FM][i] = __builtin_fmaf(pq[i], s, acc[qq % FM][qq / FM][i]);
-            };
-            auto issue_loads = [&](int j) {
+            for (int i = i0; i < i1; ++i)
+                acc[qq % FM][qq / FM][i] = __builtin_fmaf(pq[i], s, acc[qq % FM][qq / FM][i]);
+        };
+        // copy t of block kb (>= kbu): of this tile, of the next one in the tail, or a
+        // re-read of block KB-1
+        auto copy = [&](int t, uint8_t* smem, int kb, bool past) {
+            if constexpr (TAIL) {
+                if (past) issue_copy(nx, t, smem, kb - KB);
+                else issue_copy(cur, t, smem, kb);
+            } else {
+                issue_copy(cur, t, smem, kb < KB ? kb : KB - 1);
+            }
+        };
+        auto issue_loads = [&](int j) {
 #pragma unroll
-                for (int t = 0; t < NDMA; ++t) {
-                    const int g = JB + 1 + t * CPN / CPD;
-                    if (g < NJ && j == g) issue_copy(t, stage_buf[U], kbu + NST);
-                    if (g >= NJ && j == g - NJ) issue_copy(t, dst, kbu + NST - 1);
-                }
-            };
-            auto barrier = [&]() {
-                // The next block's B scales (scalar loads) are issued here, where the
-                // wave waits for all its LDS reads anyway: scalar loads complete out of
-                // order and share that counter, so while one is in flight every wait
-                // for an LDS read would have to be a wait for all of them.  The slot's
-                // previous contents were last used by promotions early in this block.
-                load_sb(scn, nkb);
-                wait_lds_all();
-                wait_vmem_le<(NST - 2) * NVM>();
-                stage_barrier();
-            };
+            for (int t = 0; t < NDMA; ++t) {
+                const int g = JB + 1 + t * CPN / CPD;
+                // in the tail every block's first-part copies are past the end, and its
+                // wrapped copies are past the end except in the tail's first block
+                if (g < NJ && j == g) copy(t, stage_buf[U], kbu + NST, true);
+                if (g >= NJ && j == g - NJ) copy(t, dst, kbu + NST - 1, U > 0);
+            }
+        };
+        auto barrier = [&]() {
+            // The next block's B scales (scalar loads) are issued here, where the
+            // wave waits for all its LDS reads anyway: scalar loads complete out of
+            // order and share that counter, so while one is in flight every wait
+            // for an LDS read would have to be a wait for all of them.  The slot's
+            // previous contents were last used by promotions early in this block.
+            // The tail's last block loads the next tile's block 0 (if any).
+            if constexpr (TAIL && U == NST - 1) {
+                load_sb(nx, scn, 0);
+            } else {
+                load_sb(cur, scn, kbu + 1 < KB ? kbu + 1 : KB - 1);
+            }
+            wait_lds_all();
+            wait_vmem_le<(NST - 2) * NVM>();
+            stage_barrier();
+        };
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int fn = j / FM, fm = j % FM;
-                const int slot = (U * NJ + j) % R;
-                if constexpr (MF == 16) {
-                    part[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[0], af[fm][0], vacc{}, 0, 0,
-                                                                                  0, 0, 0, 0);
-                    promote(j - kLag, 0, NACC);
-                    issue_loads(j);
-                    if (j == JB) barrier();
-                    if (fm == 0) bnext = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 0) : frag(ln, bcol0, 0);
-                    if (j == JB) read_sa(scn, nxt);
-                    if (fn == FN - 1) af[fm][0] = frag(ln, arow0 + fm * MF, 0);
-                    if (fm == FM - 1) bf[0] = bnext;
-                } else {
-                    part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[0], af[fm][0], vacc{}, 0, 0,
-                                                                                 0, 0, 0, 0);
-                    promote(j - kLag, 0, NACC / 2);
-                    issue_loads(j);
-                    if (j == JB) barrier();
-                    // each K half's fragments are reloaded as soon as the MFMA that
-                    // reads them for the last time in this block has been issued
-                    if (fm == FM - 1) bf[0] = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 0) : frag(ln, bcol0, 0);
-                    if (j == JB) read_sa(scn, nxt);
-                    if (fn == FN - 1) af[fm][0] = frag(ln, arow0 + fm * MF, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                    part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[1], af[fm][1], part[slot], 0,
-                                                                                 0, 0, 0, 0, 0);
-                    promote(j - kLag, NACC / 2, NACC);
-                    if (fm == FM - 1) bf[1] = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 1) : frag(ln, bcol0, 1);
-                    if (fn == FN - 1) af[fm][1] = frag(ln, arow0 + fm * MF, 1);
-                }
-                // keep this order: the scheduler would otherwise pull each promotion up
-                // against its own MFMA and stall on the result
+        for (int j = 0; j < NJ; ++j) {
+            const int fn = j / FM, fm = j % FM;
+            const int slot = (U * NJ + j) % R;
+            if constexpr (MF == 16) {
+                part[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[0], af[fm][0], vacc{}, 0, 0,
+                                                                              0, 0, 0, 0);
+                promote(j - kLag, 0, NACC);
+                issue_loads(j);
+                if (j == JB) barrier();
+                if (fm == 0) bnext = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 0) : frag(ln, bcol0, 0);
+                if (j == JB) read_sa(scn, nxt);
+                if (fn == FN - 1) af[fm][0] = frag(ln, arow0 + fm * MF, 0);
+                if (fm == FM - 1) bf[0] = bnext;
+            } else {
+                part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[0], af[fm][0], vacc{}, 0, 0,
+                                                                             0, 0, 0, 0);
+                promote(j - kLag, 0, NACC / 2);
+                issue_loads(j);
+                if (j == JB) barrier();
+                // each K half's fragments are reloaded as soon as the MFMA that
+                // reads them for the last time in this block has been issued
+                if (fm == FM - 1) bf[0] = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 0) : frag(ln, bcol0, 0);
+                if (j == JB) read_sa(scn, nxt);
+                if (fn == FN - 1) af[fm][0] = frag(ln, arow0 + fm * MF, 0);
                 __builtin_amdgcn_sched_barrier(0);
+                part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[1], af[fm][1], part[slot], 0,
+                                                                             0, 0, 0, 0, 0);
+                promote(j - kLag, NACC / 2, NACC);
+                if (fm == FM - 1) bf[1] = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 1) : frag(ln, bcol0, 1);
+                if (fn == FN - 1) af[fm][1] = frag(ln, arow0 + fm * MF, 1);
             }
-        };
-        // the partials of the last block's final kLag steps, promoted after the loop
-        auto drain = [&](auto stage_tag) {
-            constexpr int U = decltype(stage_tag)::value;
-            const Scales& sl = sc[U];
+            // keep this order: the scheduler would otherwise pull each promotion up
+            // against its own MFMA and stall on the result
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // the partials of the last block's final kLag steps, promoted after the loop
+    auto drain = [&](auto stage_tag) {
+        constexpr int U = decltype(stage_tag)::value;
+        const Scales& sl = sc[U];
 #pragma unroll
-            for (int q = NJ - kLag; q < NJ; ++q) {
-                const int fm = q % FM, fn = q / FM;
-                const float s = sl.a[fm] * pick_b(sl, fn);
-                const vacc& pq = part[(U * NJ + q) % R];
+        for (int q = NJ - kLag; q < NJ; ++q) {
+            const int fm = q % FM, fn = q / FM;
+            const float s = sl.a[fm] * pick_b(sl, fn);
+            const vacc& pq = part[(U * NJ + q) % R];
 #pragma unroll
-                for (int i = 0; i < NACC; ++i) acc[fm][fn][i] = __builtin_fmaf(pq[i], s, acc[fm][fn][i]);
-            }
-        };
+            for (int i = 0; i < NACC; ++i) acc[fm][fn][i] = __builtin_fmaf(pq[i], s, acc[fm][fn][i]);
+        }
+    };
+    // PIPE (chosen by the host when K/128 is a multiple of NST): a tile's blocks past
+    // its last one are the next tile's first blocks
+    reset_tile();
 
-        if (wave_active) {
-            // whole groups of NST blocks, then the remaining KB % NST blocks: the hot
-            // loop has a single exit, which keeps the register allocator from
-            // splitting the accumulators' live ranges around mid-body exits
+    for (;;) {
+        // the next tile's position is known from here on; its descriptors are built
+        // only where its copies start, which keeps them out of the hot loop's registers
+        const bool has_nx = advance();
+        const bool piped = PIPE && has_nx;
+        auto make_nx = [&]() {
+            if (has_nx) build_tile(nx);
+            else null_tile(nx);
+        };
+        if (cur.active) {
+            // whole groups of NST blocks (the last group is the tail when K/128 is a
+            // multiple of NST), then the remaining KB % NST blocks: the hot loop has a
+            // single exit, which keeps the register allocator from splitting the
+            // accumulators' live ranges around mid-body exits
             const int KF = KB - KB % NST;
-            for (int kb = 0; kb < KF; kb += NST)
-                static_for<0, NST>([&](auto u) { block(u, kb + decltype(u)::value); });
-            static_for<0, NST - 1>([&](auto u) {
-                if (KF + decltype(u)::value < KB) block(u, KF + decltype(u)::value);
-            });
+            if constexpr (PIPE) {
+                const int KM = KF - NST;
+                for (int kb = 0; kb < KM; kb += NST)
+                    static_for<0, NST>([&](auto u) { block(u, std::false_type{}, kb + decltype(u)::value); });
+                make_nx();
+                static_for<0, NST>([&](auto u) { block(u, std::true_type{}, KM + decltype(u)::value); });
+            } else {
+                for (int kb = 0; kb < KF; kb += NST)
+                    static_for<0, NST>([&](auto u) { block(u, std::false_type{}, kb + decltype(u)::value); });
+                static_for<0, NST - 1>([&](auto u) {
+                    if (KF + decltype(u)::value < KB) block(u, std::false_type{}, KF + decltype(u)::value);
+                });
+            }
             const int ul = (KB - 1) % NST;
             static_for<0, NST>([&](auto u) {
                 if (ul == decltype(u)::value) drain(u);
             });
         } else {
             // a wave with no valid rows (masked / short tiles) still copies its share
-            // of every stage (operands and A scales) and meets every barrier
+            // of every stage (operands and A scales) and meets every barrier; copies
+            // past the last block feed the next tile when it is pipelined
+            if constexpr (PIPE) make_nx();
             for (int kb = 0; kb < KB; kb += NST) {
 #pragma unroll
                 for (int u = 0; u < NST; ++u) {
                     if (kb + u >= KB) break;
-                    const int dkb = kb + u + NST - 1 < KB ? kb + u + NST - 1 : KB - 1;
-                    issue_stage(stage_buf[(u + NST - 1) % NST], dkb);
-                    issue_sa(stage_buf[(u + NST - 1) % NST], dkb);
+                    const int b = kb + u + NST - 1;
+                    if (b < KB) issue_stage(cur, stage_buf[(u + NST - 1) % NST], b);
+                    else if (piped) issue_stage(nx, stage_buf[(u + NST - 1) % NST], b - KB);
+                    else issue_stage(cur, stage_buf[(u + NST - 1) % NST], KB - 1);
                     wait_vmem_le<(NST - 2) * NVM>();
                     stage_barrier();
                 }
+            }
+            // ... and, like the tail of an active wave, the early copies of the next
+            // tile's block NST-1
+            if (piped) {
+#pragma unroll
+                for (int t = 0; t < NFIRST; ++t) issue_copy(nx, t, stage_buf[NST - 1], NST - 1);
             }
         }
 
@@ -645,7 +754,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         // for each pair of sub-tile columns, two lane-group swaps (V_PERMLANE16_SWAP)
         // give every lane eight adjacent columns of one sub-tile, so a store
         // instruction writes 64 contiguous bytes per row in 16-byte pieces. ----
-        if (wave_active) {
+        if (cur.active) {
             auto pack2 = [](float x, float y) -> uint32_t {
                 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
                 const v2bf t = {(__bf16)x, (__bf16)y};
@@ -654,11 +763,11 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
                 const int lr = wm * WTM + fm * MF + lsub;     // row inside the tile
-                bool row_ok = lr >= row_lo && lr < row_hi && lr < valid_rows;
+                bool row_ok = lr >= cur.row_lo && lr < cur.row_hi;
                 if constexpr (LAYOUT == kContiguous) {
-                    if (row_ok) row_ok = p.m_indices[m0 + lr] >= 0;
+                    if (row_ok) row_ok = p.m_indices[cur.m0 + lr] >= 0;
                 }
-                uint16_t* drow = d_base + (long)(m0 + (row_ok ? lr : 0)) * p.ldd;
+                uint16_t* drow = cur.d_tile + (long)(row_ok ? lr : 0) * p.ldd;
                 if constexpr (MF == 16) {
 #pragma unroll
                     for (int fn = 0; fn + 1 < FN; fn += 2) {
@@ -670,12 +779,12 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                         const auto s1 = __builtin_amdgcn_permlane16_swap(pack2(x[2], x[3]), pack2(y[2], y[3]), false,
                                                                          false);
                         // lane group g now holds sub-tile fn + (g & 1), columns 8*(g >> 1) .. +7
-                        const int col = wcol0 + (fn + (lgrp & 1)) * MF + (lgrp >> 1) * 8;
+                        const int col = cur.wcol0 + (fn + (lgrp & 1)) * MF + (lgrp >> 1) * 8;
                         if (row_ok && col < p.n) *(uint4*)(drow + col) = uint4{s0[0], s1[0], s0[1], s1[1]};
                     }
                     if constexpr (FN % 2 == 1) {
                         const vacc& x = acc[fm][FN - 1];
-                        const int col = wcol0 + (FN - 1) * MF + lgrp * 4;
+                        const int col = cur.wcol0 + (FN - 1) * MF + lgrp * 4;
                         if (row_ok && col < p.n) *(uint2*)(drow + col) = uint2{pack2(x[0], x[1]), pack2(x[2], x[3])};
                     }
                 } else {
@@ -683,7 +792,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                     for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
                         for (int q = 0; q < NACC / 4; ++q) {
-                            const int col = wcol0 + fn * MF + q * 8 + lgrp * 4;
+                            const int col = cur.wcol0 + fn * MF + q * 8 + lgrp * 4;
                             if (row_ok && col < p.n)
                                 *(uint2*)(drow + col) = uint2{pack2(acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1]),
                                                               pack2(acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3])};
@@ -692,49 +801,87 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 }
             }
         }
-        // the redundant copies issued past the last K block must land before the next
-        // tile (or another workgroup) reuses these buffers; then every wave is done
-        wait_vmem_le<0>();
-        __syncthreads();
-        }   // pass
+
+        if constexpr (PIPE) {
+            if (!has_nx) break;
+            // The next tile's first blocks are already in LDS (certified by this tile's
+            // last barrier), and an active wave has its first fragments and scales in
+            // registers; a wave that was idle reads them now.
+            const bool was_active = cur.active;
+            cur = nx;
+            reset_tile();
+            if (cur.active && !was_active) {
+                load_sb(cur, sc[0], 0);
+                first_fragments();
+            }
+        } else {
+            // the copies issued past the last K block must land before the next tile
+            // (or another workgroup) reuses these buffers; then every wave is done
+            wait_vmem_le<0>();
+            __syncthreads();
+            if (!has_nx) break;
+            build_tile(cur);
+            reset_tile();
+            prologue(cur);
+        }
     }
+    // the last tile's copies past its end (of nothing) land before the exit
+    if constexpr (PIPE) wait_vmem_le<0>();
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST>
-static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST>), dim3(grid), dim3(WM * WN * 64), 0, s, p, p.a,
-                       p.sa, p.b, p.sb, p.d);
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE>
+static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE>), dim3(grid), dim3(WM * WN * 64), 0, s, p,
+                       p.a, p.sa, p.b, p.sb, p.d);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST>
-static hipError_t occupancy_cfg(int* blocks) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks, reinterpret_cast<const void*>(&dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST>), WM * WN * 64, 0);
+// The pipelined variant runs the next tile's first NST blocks as the tail of the
+// current one, which needs the K blocks to split into whole groups of NST.  It is
+// compiled only for the configurations whose registers it fits (PIPE_OK).
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK>
+static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
+    if constexpr (PIPE_OK) {
+        if (p.kblocks % NST == 0) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, true>(p, grid, s);
+    }
+    return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false>(p, grid, s);
 }
 
-#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF)                                 \
-    {ID, LAYOUT, BM, BN, WM, WN, EFF, &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST>,       \
-     &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF, NST>}
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK>
+static hipError_t occupancy_cfg(int* blocks) {
+    typedef void (*KernelFn)(const GemmParams, const uint8_t*, const float*, const uint8_t*, const float*, uint16_t*);
+    const KernelFn k0 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, false>;
+    const KernelFn k1 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>;
+    int b0 = 0, b1 = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, reinterpret_cast<const void*>(k0), WM * WN * 64, 0);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, reinterpret_cast<const void*>(k1), WM * WN * 64, 0);
+    *blocks = b0 < b1 ? b0 : b1;
+    return e;
+}
+
+#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF, PIPE_OK)                            \
+    {ID, LAYOUT, BM, BN, WM, WN, EFF, &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>,  \
+     &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>}
 
 static const KernelConfig kConfigs[] = {
     // dense
-    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 2, 1.00),
-    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 2, 0.90),
-    DG_CFG(2, kDense, 128, 128, 2, 2, 16, 4, 0.55),
-    DG_CFG(3, kDense, 64, 112, 4, 1, 16, 4, 0.35),
-    DG_CFG(4, kDense, 128, 224, 4, 2, 16, 3, 0.80),
+    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 2, 1.00, true),
+    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 2, 0.90, true),
+    DG_CFG(2, kDense, 128, 128, 2, 2, 16, 4, 0.55, false),
+    DG_CFG(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false),
+    DG_CFG(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true),
     // contiguous (BLOCK_M = the 128-row segment alignment)
-    DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00),
-    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55),
-    DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95),
-    DG_CFG(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30),
+    DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false),
+    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false),
+    DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95, true),
+    DG_CFG(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false),
     // masked
-    DG_CFG(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00),
-    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00),
-    DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90),
-    DG_CFG(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90),
-    DG_CFG(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10),
+    DG_CFG(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false),
+    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false),
+    DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false),
+    DG_CFG(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90, false),
+    DG_CFG(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false),
 };
 
 const KernelConfig* kernel_configs(int* count) {

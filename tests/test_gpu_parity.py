@@ -113,6 +113,24 @@ def test_dense_cu_cap_is_bit_identical(orc):
     check_values(base, oracle_dense(orc, dd), "dense 512x1024x512")
 
 
+@pytest.mark.parametrize("k", [512, 640, 768])
+def test_dense_chained_tiles_all_configs(orc, k):
+    """Three workgroups, many tiles each: where K/128 splits into whole groups of a
+    config's LDS stages, each tile's last blocks already fetch the next tile's first
+    ones.  Ragged M and N put partial tiles and idle waves into the chains."""
+    dd = W.make_dense(300, 464, k, seed=k + 5)
+    ref = oracle_dense(orc, dd)
+    dg.dg_set_num_cus(3)
+    try:
+        for cfg in configs_of(0):
+            say(f"dense 300x464x{k} cfg={cfg} cu cap 3")
+            out, full = run_dense(dd, cfg)
+            check_values(out, ref, f"dense 300x464x{k} cfg{cfg} chained")
+            assert np.all(full[:, 464:] == W.SENTINEL_BF16)
+    finally:
+        dg.dg_set_num_cus(0)
+
+
 # --------------------------------------------------------------------------- contiguous
 def run_contiguous(cd, cfg=-1):
     import torch
@@ -154,6 +172,26 @@ def test_contiguous_small_all_configs(orc):
         if c:
             assert np.array_equal(dense_gpu_segment(cd, g, off, off + c), outs[0][off:off + c])
         off += p
+
+
+@pytest.mark.parametrize("k", [512, 768])
+def test_contiguous_chained_tiles_all_configs(orc, k):
+    """Contiguous layout with three workgroups: chains of tiles that mix one-group tiles,
+    two-group tiles (two passes) and padding, with and without next-tile prefetch."""
+    counts = [130, 0, 1, 257, 128, 40]
+    cd = W.make_contiguous(counts, n=400, k=k, seed=k + 9)
+    sentinel = np.full((cd["m_total"], 400), W.SENTINEL_BF16, np.uint16)
+    ref = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], cd["m_indices"], d_init=sentinel)
+    valid = cd["m_indices"] >= 0
+    dg.dg_set_num_cus(3)
+    try:
+        for cfg in configs_of(1):
+            say(f"contiguous counts={counts} k={k} cfg={cfg} cu cap 3")
+            out = run_contiguous(cd, cfg)
+            check_values(out[valid], ref[valid], f"contiguous k={k} cfg{cfg} chained")
+            assert np.all(out[~valid] == W.SENTINEL_BF16), "a padding row was written"
+    finally:
+        dg.dg_set_num_cus(0)
 
 
 def test_contiguous_workload_sampled(orc):
