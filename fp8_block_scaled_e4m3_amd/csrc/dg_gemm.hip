@@ -17,19 +17,20 @@
 //    one scale product sA[m]*sB[nb] serves four FMAs and sB is a wave-uniform
 //    scalar for each 16-column sub-tile (16 divides 128, so a sub-tile never
 //    straddles two B scale blocks even when BLOCK_N is not a power of two).
-//  * Operand tiles (BLOCK_M + BLOCK_N rows of 128 K-bytes) go global -> LDS with
-//    16-byte direct-to-LDS loads, two stages (one K block in flight while the
-//    other is consumed), rows XOR-swizzled in 16-byte chunks so that the
-//    MFMA-fragment reads are bank-conflict free.
+//  * Operand tiles (BLOCK_M + BLOCK_N rows of 128 K-bytes) and the tile's A
+//    scales go global -> LDS with direct-to-LDS buffer loads into 2..4 stages (the
+//    copies of a K block are issued as soon as the stage it reuses is free), rows
+//    XOR-swizzled in 16-byte chunks so that the MFMA-fragment reads are bank-
+//    conflict free.  B scales are wave-uniform scalar loads.
 //  * A persistent grid walks the tile list.  Tiles are handed out so that the
 //    workgroups resident on one XCD (dispatch is round-robin over the 8 XCDs)
 //    work on a compact block of the output and share A and B through that
 //    XCD's L2.  Contiguous tiles look up their group in m_indices; masked tiles
 //    are enumerated on the device from masked_m (the host never reads it), so
 //    only row blocks that hold valid rows are visited.
-//  * The epilogue converts to BF16 with the hardware RNE convert and stores
-//    8 bytes per lane; padding rows (contiguous) and rows >= masked_m (masked)
-//    are never written.
+//  * The epilogue converts to BF16 with the hardware RNE convert; lane-group
+//    swaps give each lane eight adjacent columns, stored 16 bytes at a time.
+//    Padding rows (contiguous) and rows >= masked_m (masked) are never written.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,8 +42,6 @@ namespace dg {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) const v4i lds_v4i;
@@ -68,16 +67,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
 // function, so that only the device compilation ever checks the 16-byte form).
 __device__ __forceinline__ void buffer_copy_lds16(__amdgpu_buffer_rsrc_t rs, lds_void* dst, int voff, int soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 0);
-}
-
-// One fp32 from a buffer (per-lane byte offset + scalar byte offset).
-__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-
-// A value every lane holds identically, moved to a scalar register.
-__device__ __forceinline__ float uniform(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
 // Workgroup barrier without a memory fence.  __syncthreads() also fences, which
@@ -136,6 +125,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "block rows must be a multiple of 8");
     static_assert(WTN <= 256, "a wave's columns touch at most three B scale blocks");
+    static_assert(MF != 16 || WTN <= 128, "16-wide sub-tiles: a wave's columns touch at most two B scale blocks");
     static_assert(WTM <= 64, "one 4-byte-per-lane copy carries a wave's A scales");
     typedef float vacc __attribute__((ext_vector_type(NACC)));
 
