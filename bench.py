@@ -26,6 +26,7 @@ METRIC = "FP8 TFLOPS (% of MI355X FP8 MFMA peak); GB/s (% HBM) for masked decode
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 HEADLINE = "dense_m4096_n7168_k7168"
+CU_CAPS = (224, 192, 128)       # CU caps the masked decode call is also timed under
 KERNEL_SRC = os.path.join(ROOT, "fp8_block_scaled_e4m3_amd", "csrc", "dg_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -313,6 +314,18 @@ def main():
                          "traffic": traffic_for(name)}
             if ww.kind == "masked":
                 sec[name]["sum_masked_m"] = int(np.clip(d2["masked_m"], 0, ww.max_m).sum())
+                # the decode GEMM sharing the GPU with a communication kernel: the same
+                # call restricted to fewer CUs (dg_set_num_cus), the rest left free
+                capped = {}
+                for cap in CU_CAPS:
+                    dg.dg_set_num_cus(cap)
+                    try:
+                        c2()
+                        cs, _ = time_launches(c2, args.secondary_iters, flush)
+                    finally:
+                        dg.dg_set_num_cus(0)
+                    capped[str(cap)] = {"us": round(cs * 1e6, 2), "gbps": round(b2 / cs / 1e9, 1)}
+                sec[name]["cu_capped"] = capped
             del d2, v2, o2, c2
             torch.cuda.empty_cache()
         sec.update(time_casts(args.secondary_iters, flush))

@@ -111,7 +111,7 @@ bool better(double cost, long waves, double best_cost, long best_waves) {
 }
 
 // Pick among the compiled configurations of one layout.
-int choose_config(int layout, int m, int n, int num_units, const DeviceInfo* dev, int max_m_hint) {
+int choose_config(int layout, int m, int n, int num_groups, int num_units, const DeviceInfo* dev, int max_m_hint) {
     int count = 0;
     const KernelConfig* cfgs = dg::kernel_configs(&count);
     const int forced = g_forced_cfg[layout].load();
@@ -122,17 +122,14 @@ int choose_config(int layout, int m, int n, int num_units, const DeviceInfo* dev
     for (int i = 0; i < count; ++i) {
         const KernelConfig& c = cfgs[i];
         if (c.layout != layout) continue;
-        if (layout == dg::kMasked) {
-            // the whole capacity in one row block when it fits (B is then streamed once
-            // per group), else the largest block; among those the most efficient shape
-            const int want = max_m_hint <= 128 ? 128 : 256;
-            if (c.bm != want) continue;
-            if (best < 0 || c.eff > cfgs[best].eff) best = i;
-            continue;
-        }
+        // Masked: the whole capacity in one row block when it fits (B is then streamed
+        // once per group), else the largest block; among those the cost model below on
+        // the upper bound of the tile count (every group full), so that a CU cap that
+        // leaves fewer CUs than 256x256 tiles picks narrower tiles.
+        if (layout == dg::kMasked && c.bm != (max_m_hint <= 128 ? 128 : 256)) continue;
         // The busiest CU's share: ceil(tiles / CUs) tiles of bm x bn at the shape's
         // relative throughput (workgroups resident together share one CU).
-        const long tiles = ceil_div(m, c.bm) * ceil_div(n, c.bn);
+        const long tiles = (layout == dg::kMasked ? num_groups : 1) * ceil_div(m, c.bm) * ceil_div(n, c.bn);
         const long waves = ceil_div(tiles, (long)num_units);
         const double cost = (double)waves * c.bm * c.bn / c.eff;
         if (best < 0 || better(cost, waves, best_cost, best_waves)) {
@@ -156,7 +153,7 @@ int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_
     }
     int count = 0;
     const KernelConfig* cfgs = dg::kernel_configs(&count);
-    const int ci = choose_config(layout, m_for_plan, p.n, units, dev, max_m_hint);
+    const int ci = choose_config(layout, m_for_plan, p.n, p.num_groups, units, dev, max_m_hint);
     if (ci < 0) return DG_ERR_UNSUPPORTED;
     const KernelConfig& c = cfgs[ci];
     const int per_cu = dev ? dev->occ[ci] : 1;

@@ -126,6 +126,10 @@ def test_describe_launch_shapes():
     assert (d["block_m"], d["block_n"], d["tiles"]) == (256, 256, 130 * 16)
     d = dg.dg_describe_launch(2, 256, 4096, 7168, 16, 256)
     assert d["block_m"] == 256 and d["tiles"] == 16 * 4096 // d["block_n"]
+    # a CU cap below the 256 tiles of 256x256 picks the narrower tiles (fewer rounds)
+    assert (d["block_n"], d["grid"]) == (256, 256)
+    d = dg.dg_describe_launch(2, 256, 4096, 7168, 16, 224)
+    assert (d["block_m"], d["block_n"], d["grid"]) == (256, 128, 224)
 
 
 def test_quantize_validation(lib):

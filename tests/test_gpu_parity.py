@@ -131,6 +131,16 @@ def test_dense_chained_tiles_all_configs(orc, k):
         dg.dg_set_num_cus(0)
 
 
+def test_dense_per_tensor_scaling(orc):
+    """Per-tensor scaling is the special case of one value in every scale block: the
+    same kernel, checked against the oracle with constant sA and sB."""
+    dd = W.make_dense(384, 640, 1024, seed=31)
+    dd["sa"] = np.full_like(dd["sa"], 0.0078125 * 3)
+    dd["sb"] = np.full_like(dd["sb"], 1.5)
+    out, _ = run_dense(dd)
+    check_values(out, oracle_dense(orc, dd), "dense per-tensor scales")
+
+
 # --------------------------------------------------------------------------- contiguous
 def run_contiguous(cd, cfg=-1):
     import torch
