@@ -212,7 +212,11 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // sA read zeros).
     const uint32_t sa_voff = (uint32_t)(wm * WTM + lane) * 4u;
     const int sa_lds = ROWS * kKBlock + wave * 256 + lsub * 4;   // this lane's row, sub-tile 0
-    constexpr int NSB = MF == 16 ? 2 : FN;
+    // B scale rows a wave reads per K block: MF=16 sub-tiles need at most two (the
+    // wave's columns span at most 128); a 128-column wave tile at a multiple of 128
+    // needs exactly one, so all of its sub-tiles share one scale product per row
+    constexpr bool ONE_SB = MF == 16 && WTN == kKBlock && BN % kKBlock == 0;
+    constexpr int NSB = MF == 16 ? (ONE_SB ? 1 : 2) : FN;
 
     // ---- one tile (or one pass of a two-group contiguous tile): everything its
     // copies, scales and epilogue need, all wave-uniform ----
@@ -342,10 +346,12 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         if constexpr (MF == 16) {
             const int nb_lo = min(t.wcol0 / kKBlock, p.nblocks - 1);
             t.sb_off[0] = nb_lo * KB * 4;
-            t.sb_off[1] = min(nb_lo + 1, p.nblocks - 1) * KB * 4;
+            if constexpr (!ONE_SB) {
+                t.sb_off[NSB - 1] = min(nb_lo + 1, p.nblocks - 1) * KB * 4;
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-                if ((t.wcol0 + fn * MF) / kKBlock > nb_lo) t.hi_mask |= 1u << fn;
+                for (int fn = 0; fn < FN; ++fn)
+                    if ((t.wcol0 + fn * MF) / kKBlock > nb_lo) t.hi_mask |= 1u << fn;
+            }
         } else {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
@@ -428,7 +434,9 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // the B scale of sub-tile column fn as a scalar: MF=16 picks the wave's low or
     // high scale row with uniform integer operations
     auto pick_b = [&](const Scales& sc, int fn) -> float {
-        if constexpr (MF == 16) {
+        if constexpr (ONE_SB) {
+            return sc.b[0];
+        } else if constexpr (MF == 16) {
             const unsigned m = 0u - ((cur.hi_mask >> fn) & 1u);
             const unsigned lo = __builtin_bit_cast(unsigned, sc.b[0]);
             const unsigned hi = __builtin_bit_cast(unsigned, sc.b[NSB - 1]);
