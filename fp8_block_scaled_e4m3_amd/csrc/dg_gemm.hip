@@ -869,6 +869,7 @@ static const KernelConfig kConfigs[] = {
     DG_CFG(2, kDense, 128, 128, 2, 2, 16, 4, 0.55, false),
     DG_CFG(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false),
     DG_CFG(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true),
+    DG_CFG(5, kDense, 256, 256, 4, 2, 16, 2, 1.15, true),
     // contiguous (BLOCK_M = the 128-row segment alignment)
     DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false),
     DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false),

@@ -118,8 +118,10 @@ def test_plan_fills_256_cus():
 
 
 def test_describe_launch_shapes():
+    # 256x256 tiles (one B scale row per wave) beat 256x224 (two whole rounds) in the
+    # planner's model: 448 tiles, the second round three quarters full
     d = dg.dg_describe_launch(0, 4096, 7168, 7168, 1, 256)
-    assert (d["block_m"], d["block_n"], d["tiles"]) == (256, 224, 512) and d["grid"] == 256
+    assert (d["block_m"], d["block_n"], d["tiles"]) == (256, 256, 448) and d["grid"] == 256
     d = dg.dg_describe_launch(0, 256, 7168, 2048, 1, 256)
     assert (d["block_m"], d["block_n"], d["tiles"]) == (64, 112, 256)
     d = dg.dg_describe_launch(1, 33280, 4096, 7168, 8, 256)
