@@ -88,6 +88,10 @@ __device__ __forceinline__ void wait_vmem_le() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Lambdas of the kernel are always inlined: a call that stays out of line would put
+// the accumulator arrays it captures by reference into scratch memory.
+#define DG_INLINE __attribute__((always_inline))
+
 // f(integral_constant<I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -234,7 +238,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // tile holding two groups yields two passes
     int step = 0, pass = 0, npass = 0, st_m0 = 0, st_n0 = 0, st_vr = 0;
     int pg[2] = {0, 0}, plo[2] = {0, 0}, phi[2] = {BM, BM};
-    auto fetch_step = [&]() -> bool {   // from `step` on, the first step with work
+    auto fetch_step = [&]() DG_INLINE -> bool {   // from `step` on, the first step with work
         for (;; ++step) {
             if (step * P >= total_tiles) return false;
             // ---- tile index: XCD-aware hand-out of the linear tile order ----
@@ -284,7 +288,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             // segment blocks that belong to different groups is computed in two passes,
             // one per group, each keeping only its own rows.
             if constexpr (LAYOUT == kContiguous) {
-                auto group_at = [&](int r) {
+                auto group_at = [&](int r) DG_INLINE {
                     if (r >= valid_rows) return -1;
                     const int v = p.m_indices[st_m0 + r];
                     return (v < 0 || v >= p.num_groups) ? -1 : v;
@@ -317,7 +321,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         }
     };
     // the tile the hand-out state describes
-    auto build_tile = [&](Tile& t) {
+    auto build_tile = [&](Tile& t) DG_INLINE {
         const int g = pass == 0 ? pg[0] : pg[1];
         const int m0 = st_m0, n0 = st_n0, valid_rows = st_vr;
         t.m0 = m0;
@@ -360,7 +364,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         t.active = wm * WTM < t.row_hi && wm * WTM + WTM > t.row_lo;
     };
     // no tile: its copies read nothing (every lane is out of range) and write zeros
-    auto null_tile = [&](Tile& t) {
+    auto null_tile = [&](Tile& t) DG_INLINE {
         t.m0 = t.row_lo = t.row_hi = t.wcol0 = 0;
         t.hi_mask = 0;
 #pragma unroll
@@ -371,7 +375,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         t.d_tile = d_ptr;
     };
     // move the hand-out state to the tile after the current one; false when none is left
-    auto advance = [&]() -> bool {
+    auto advance = [&]() DG_INLINE -> bool {
         if (pass + 1 < npass) {
             ++pass;
             return true;
@@ -388,7 +392,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // DMA slot t of this wave (A slots first, then B slots) for K block kb of tile
     // tl.  A slot index past the last one repeats the last slot: the same bytes land
     // on the same LDS location twice, which keeps the issue free of branches.
-    auto issue_slot = [&](const Tile& tl, uint8_t* smem, int kb, int t) {
+    auto issue_slot = [&](const Tile& tl, uint8_t* smem, int kb, int t) DG_INLINE {
         const int koff = kb * kKBlock;
         if (t < A_PER) {
             const int j = min(wave + t * NW, A_SLOTS - 1);
@@ -398,12 +402,12 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             buffer_copy_lds16(tl.rs_b, (lds_void*)(smem + BM * kKBlock + j * 1024), (int)b_off[t - A_PER], koff);
         }
     };
-    auto issue_sa = [&](const Tile& tl, uint8_t* smem, int kb) {
+    auto issue_sa = [&](const Tile& tl, uint8_t* smem, int kb) DG_INLINE {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(tl.rs_sa,
                                                  (lds_void*)(smem + ROWS * kKBlock + wave * 256), 4,
                                                  (int)(sa_voff + (uint32_t)(kb * p.ld_sa) * 4u), 0, 0, 0);
     };
-    auto issue_stage = [&](const Tile& tl, uint8_t* smem, int kb) {
+    auto issue_stage = [&](const Tile& tl, uint8_t* smem, int kb) DG_INLINE {
 #pragma unroll
         for (int t = 0; t < NSLOT; ++t) issue_slot(tl, smem, kb, t);
         issue_sa(tl, smem, kb);
@@ -422,18 +426,18 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // Scales of one K block: a[fm] per lane (its row of sub-tile row fm), b[t]
     // wave-uniform (scalar loads of sB, which never pass through the texture unit)
     struct Scales { float a[FM]; float b[NSB]; };
-    auto load_sb = [&](const Tile& tl, Scales& sc, int kb) {
+    auto load_sb = [&](const Tile& tl, Scales& sc, int kb) DG_INLINE {
 #pragma unroll
         for (int t = 0; t < NSB; ++t) sc.b[t] = tl.sb_grp[(tl.sb_off[t] >> 2) + kb];
     };
-    auto read_sa = [&](Scales& sc, const uint8_t* smem) {
+    auto read_sa = [&](Scales& sc, const uint8_t* smem) DG_INLINE {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
             sc.a[fm] = *(const lds_f32*)((const lds_u8*)smem + sa_lds + fm * MF * 4);
     };
     // the B scale of sub-tile column fn as a scalar: MF=16 picks the wave's low or
     // high scale row with uniform integer operations
-    auto pick_b = [&](const Scales& sc, int fn) -> float {
+    auto pick_b = [&](const Scales& sc, int fn) DG_INLINE -> float {
         if constexpr (ONE_SB) {
             return sc.b[0];
         } else if constexpr (MF == 16) {
@@ -490,55 +494,73 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     static_assert(kLag <= JB, "the previous block's scales are dead by the barrier");
     // copy t of block kb of tile tl into stage smem (blocks past the last one of a
     // tile that is not followed by pipelined work re-read block KB-1)
-    auto issue_copy = [&](const Tile& tl, int t, uint8_t* smem, int kb) {
+    auto issue_copy = [&](const Tile& tl, int t, uint8_t* smem, int kb) DG_INLINE {
         if (t < NSLOT) issue_slot(tl, smem, kb, t);
         else issue_sa(tl, smem, kb);
     };
 
     Scales sc[NST];
-    uint8_t* const stage_buf[8] = {smem0, smem1, smem2, smem3, smem4, smem5, smem6, smem7};
+    // stage i's buffer; every index is a compile-time constant (no array of stage
+    // pointers exists, so nothing can index one at run time)
+    auto stage = [&](auto idx) -> uint8_t* {
+        constexpr int i = decltype(idx)::value;
+        static_assert(i >= 0 && i < NST, "stage index");
+        if constexpr (i == 0) return smem0;
+        else if constexpr (i == 1) return smem1;
+        else if constexpr (i == 2) return smem2;
+        else if constexpr (i == 3) return smem3;
+        else if constexpr (i == 4) return smem4;
+        else if constexpr (i == 5) return smem5;
+        else if constexpr (i == 6) return smem6;
+        else return smem7;
+    };
+    using std::integral_constant;
     constexpr int NH = MF == 32 ? 2 : 1;
     v8i af[FM][NH], bf[NH], bnext;
     vacc part[R];
     vacc acc[FM][FN];
     const int arow0 = wm * WTM, bcol0 = BM + wn * WTN;
 
-    // This lane's byte offsets in a stage, made opaque to the compiler so that
-    // every fragment read is stage + offset + an immediate row offset instead
-    // of a separately hoisted address register per fragment and stage.  Only
-    // the offset is hidden: the stage array stays visible, so the compiler
-    // knows which stage a read touches and that it is not one the copies fill.
-    auto lane_base = [&](const uint8_t* smem, lds_u8* (&lb)[2][2]) {
+    // This lane's byte offsets in a stage from the first row of the wave's A or B
+    // rows, made opaque to the compiler so that every fragment read is stage +
+    // offset + an immediate row offset (no per-read address arithmetic, and no
+    // separately hoisted address register per fragment and stage).  Only the
+    // offset is hidden: the stage array stays visible, so the compiler knows
+    // which stage a read touches and that it is not one the copies fill.
+    auto lane_base = [&](const uint8_t* smem, int row_base, lds_u8* (&lb)[2][2]) DG_INLINE {
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                int off = lsub * kKBlock + coff[h][e];
+                int off = (row_base + lsub) * kKBlock + coff[h][e];
                 asm volatile("" : "+v"(off));
                 lb[h][e] = (lds_u8*)smem + off;
             }
     };
-    // fragment of sub-tile rows [row0, row0+MF) for K half h (MF=16: whole block)
-    auto frag = [&](lds_u8* const (&lb)[2][2], int row0, int h) -> v8i {
+    // fragment of sub-tile rows [row0, row0+MF) past the lane base's first row, for
+    // K half h (MF=16: whole block)
+    auto frag = [&](lds_u8* const (&lb)[2][2], int row0, int h) DG_INLINE -> v8i {
         const v4i lo = *(const lds_v4i*)(lb[h][0] + row0 * kKBlock);
         const v4i hi = *(const lds_v4i*)(lb[h][1] + row0 * kKBlock);
         return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     };
     // the first block's fragments and scales of a tile, from stage 0 (read in the
     // order the loop issues a next block's reads: B fragment, A scales, A fragments)
-    auto first_fragments = [&]() {
+    auto first_fragments = [&]() DG_INLINE {
+        lds_u8* la[2][2];
         lds_u8* lb[2][2];
-        lane_base(smem0, lb);
+        lane_base(smem0, arow0, la);
+        lane_base(smem0, bcol0, lb);
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-            bf[h] = frag(lb, bcol0, h);
+            bf[h] = frag(lb, 0, h);
             if (h == 0) read_sa(sc[0], smem0);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) af[fm][h] = frag(lb, arow0 + fm * MF, h);
+            for (int fm = 0; fm < FM; ++fm) af[fm][h] = frag(la, fm * MF, h);
         }
     };
     // tile start: the "previous block" of block 0 has zero partials and zero scales
-    auto reset_tile = [&]() {
+    auto reset_tile = [&]() DG_INLINE {
 #pragma unroll
         for (int r = 0; r < R; ++r) part[r] = vacc{};
 #pragma unroll
@@ -553,11 +575,14 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
 
     // ---- prologue of the first tile: copies of blocks 0 .. NST-2 and the early
     // part of block NST-1's (clamped), then the first block's fragments and scales ----
-    auto prologue = [&](const Tile& tl) {
+    auto prologue = [&](const Tile& tl) DG_INLINE {
+        static_for<0, NST - 1>([&](auto ss) DG_INLINE {
+            constexpr int s = decltype(ss)::value;
+            issue_stage(tl, stage(ss), s < KB ? s : KB - 1);
+        });
 #pragma unroll
-        for (int s = 0; s < NST - 1; ++s) issue_stage(tl, stage_buf[s], s < KB ? s : KB - 1);
-#pragma unroll
-        for (int t = 0; t < NFIRST; ++t) issue_copy(tl, t, stage_buf[NST - 1], NST - 1 < KB ? NST - 1 : KB - 1);
+        for (int t = 0; t < NFIRST; ++t)
+            issue_copy(tl, t, stage(integral_constant<int, NST - 1>{}), NST - 1 < KB ? NST - 1 : KB - 1);
         // (the scalar loads complete before the loop, so the loop starts with only LDS
         // reads in flight)
         if (tl.active) load_sb(tl, sc[0], 0);
@@ -572,24 +597,26 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // last NST blocks of a tile whose K/128 is a multiple of NST; its copies past
     // the last block go to the next tile `nx` (blocks kb - KB; a null tile reads
     // nothing).  Otherwise copies past the last block re-read block KB-1.
-    auto block = [&](auto stage_tag, auto tail_tag, int kbu) {
+    auto block = [&](auto stage_tag, auto tail_tag, int kbu) DG_INLINE {
         constexpr int U = decltype(stage_tag)::value;
         constexpr bool TAIL = decltype(tail_tag)::value;
-        const uint8_t* curs = stage_buf[U];
-        const uint8_t* nxt = stage_buf[(U + 1) % NST];
-        uint8_t* dst = stage_buf[(U + NST - 1) % NST];
+        uint8_t* const curs = stage(integral_constant<int, U>{});
+        const uint8_t* nxt = stage(integral_constant<int, (U + 1) % NST>{});
+        uint8_t* dst = stage(integral_constant<int, (U + NST - 1) % NST>{});
         const Scales& scs = sc[U];
         const Scales& scp = sc[(U + NST - 1) % NST];   // previous block's
         Scales& scn = sc[(U + 1) % NST];               // next block's (for NST=2: scp's slot)
-        lds_u8* lc[2][2];
-        lds_u8* ln[2][2];
-        lane_base(curs, lc);
-        lane_base(nxt, ln);
-        auto scale = [&](bool prev, int fm, int fn) {
+        lds_u8* lc[2][2];    // B rows of this block's stage
+        lds_u8* ln[2][2];    // B rows of the next block's stage
+        lds_u8* lna[2][2];   // A rows of the next block's stage
+        lane_base(curs, bcol0, lc);
+        lane_base(nxt, bcol0, ln);
+        lane_base(nxt, arow0, lna);
+        auto scale = [&](bool prev, int fm, int fn) DG_INLINE {
             const Scales& sc = prev ? scp : scs;
             return sc.a[fm] * pick_b(sc, fn);
         };
-        auto promote = [&](int q, int i0, int i1) {
+        auto promote = [&](int q, int i0, int i1) DG_INLINE {
             // q: step index relative to this block, possibly negative (previous block)
             const int slot = ((U * NJ + q) % R + R) % R;
             const int qq = q < 0 ? q + NJ : q;
@@ -601,7 +628,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         };
         // copy t of block kb (>= kbu): of this tile, of the next one in the tail, or a
         // re-read of block KB-1
-        auto copy = [&](int t, uint8_t* smem, int kb, bool past) {
+        auto copy = [&](int t, uint8_t* smem, int kb, bool past) DG_INLINE {
             if constexpr (TAIL) {
                 if (past) issue_copy(nx, t, smem, kb - KB);
                 else issue_copy(cur, t, smem, kb);
@@ -609,17 +636,17 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 issue_copy(cur, t, smem, kb < KB ? kb : KB - 1);
             }
         };
-        auto issue_loads = [&](int j) {
+        auto issue_loads = [&](int j) DG_INLINE {
 #pragma unroll
             for (int t = 0; t < NDMA; ++t) {
                 const int g = JB + 1 + t * CPN / CPD;
                 // in the tail every block's first-part copies are past the end, and its
                 // wrapped copies are past the end except in the tail's first block
-                if (g < NJ && j == g) copy(t, stage_buf[U], kbu + NST, true);
+                if (g < NJ && j == g) copy(t, curs, kbu + NST, true);
                 if (g >= NJ && j == g - NJ) copy(t, dst, kbu + NST - 1, U > 0);
             }
         };
-        auto barrier = [&]() {
+        auto barrier = [&]() DG_INLINE {
             // The next block's B scales (scalar loads) are issued here, where the
             // wave waits for all its LDS reads anyway: scalar loads complete out of
             // order and share that counter, so while one is in flight every wait
@@ -645,9 +672,9 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 promote(j - kLag, 0, NACC);
                 issue_loads(j);
                 if (j == JB) barrier();
-                if (fm == 0) bnext = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 0) : frag(ln, bcol0, 0);
+                if (fm == 0) bnext = fn + 1 < FN ? frag(lc, (fn + 1) * MF, 0) : frag(ln, 0, 0);
                 if (j == JB) read_sa(scn, nxt);
-                if (fn == FN - 1) af[fm][0] = frag(ln, arow0 + fm * MF, 0);
+                if (fn == FN - 1) af[fm][0] = frag(lna, fm * MF, 0);
                 if (fm == FM - 1) bf[0] = bnext;
             } else {
                 part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[0], af[fm][0], vacc{}, 0, 0,
@@ -657,15 +684,15 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 if (j == JB) barrier();
                 // each K half's fragments are reloaded as soon as the MFMA that
                 // reads them for the last time in this block has been issued
-                if (fm == FM - 1) bf[0] = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 0) : frag(ln, bcol0, 0);
+                if (fm == FM - 1) bf[0] = fn + 1 < FN ? frag(lc, (fn + 1) * MF, 0) : frag(ln, 0, 0);
                 if (j == JB) read_sa(scn, nxt);
-                if (fn == FN - 1) af[fm][0] = frag(ln, arow0 + fm * MF, 0);
+                if (fn == FN - 1) af[fm][0] = frag(lna, fm * MF, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[1], af[fm][1], part[slot], 0,
                                                                              0, 0, 0, 0, 0);
                 promote(j - kLag, NACC / 2, NACC);
-                if (fm == FM - 1) bf[1] = fn + 1 < FN ? frag(lc, bcol0 + (fn + 1) * MF, 1) : frag(ln, bcol0, 1);
-                if (fn == FN - 1) af[fm][1] = frag(ln, arow0 + fm * MF, 1);
+                if (fm == FM - 1) bf[1] = fn + 1 < FN ? frag(lc, (fn + 1) * MF, 1) : frag(ln, 0, 1);
+                if (fn == FN - 1) af[fm][1] = frag(lna, fm * MF, 1);
             }
             // keep this order: the scheduler would otherwise pull each promotion up
             // against its own MFMA and stall on the result
@@ -673,7 +700,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         }
     };
     // the partials of the last block's final kLag steps, promoted after the loop
-    auto drain = [&](auto stage_tag) {
+    auto drain = [&](auto stage_tag) DG_INLINE {
         constexpr int U = decltype(stage_tag)::value;
         const Scales& sl = sc[U];
 #pragma unroll
@@ -694,7 +721,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         // only where its copies start, which keeps them out of the hot loop's registers
         const bool has_nx = advance();
         const bool piped = PIPE && has_nx;
-        auto make_nx = [&]() {
+        auto make_nx = [&]() DG_INLINE {
             if (has_nx) build_tile(nx);
             else null_tile(nx);
         };
@@ -707,18 +734,18 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             if constexpr (PIPE) {
                 const int KM = KF - NST;
                 for (int kb = 0; kb < KM; kb += NST)
-                    static_for<0, NST>([&](auto u) { block(u, std::false_type{}, kb + decltype(u)::value); });
+                    static_for<0, NST>([&](auto u) DG_INLINE { block(u, std::false_type{}, kb + decltype(u)::value); });
                 make_nx();
-                static_for<0, NST>([&](auto u) { block(u, std::true_type{}, KM + decltype(u)::value); });
+                static_for<0, NST>([&](auto u) DG_INLINE { block(u, std::true_type{}, KM + decltype(u)::value); });
             } else {
                 for (int kb = 0; kb < KF; kb += NST)
-                    static_for<0, NST>([&](auto u) { block(u, std::false_type{}, kb + decltype(u)::value); });
-                static_for<0, NST - 1>([&](auto u) {
+                    static_for<0, NST>([&](auto u) DG_INLINE { block(u, std::false_type{}, kb + decltype(u)::value); });
+                static_for<0, NST - 1>([&](auto u) DG_INLINE {
                     if (KF + decltype(u)::value < KB) block(u, std::false_type{}, KF + decltype(u)::value);
                 });
             }
             const int ul = (KB - 1) % NST;
-            static_for<0, NST>([&](auto u) {
+            static_for<0, NST>([&](auto u) DG_INLINE {
                 if (ul == decltype(u)::value) drain(u);
             });
         } else {
@@ -727,22 +754,24 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             // past the last block feed the next tile when it is pipelined
             if constexpr (PIPE) make_nx();
             for (int kb = 0; kb < KB; kb += NST) {
-#pragma unroll
-                for (int u = 0; u < NST; ++u) {
-                    if (kb + u >= KB) break;
-                    const int b = kb + u + NST - 1;
-                    if (b < KB) issue_stage(cur, stage_buf[(u + NST - 1) % NST], b);
-                    else if (piped) issue_stage(nx, stage_buf[(u + NST - 1) % NST], b - KB);
-                    else issue_stage(cur, stage_buf[(u + NST - 1) % NST], KB - 1);
-                    wait_vmem_le<(NST - 2) * NVM>();
-                    stage_barrier();
-                }
+                static_for<0, NST>([&](auto uu) DG_INLINE {
+                    constexpr int u = decltype(uu)::value;
+                    if (kb + u < KB) {
+                        uint8_t* const st = stage(integral_constant<int, (u + NST - 1) % NST>{});
+                        const int b = kb + u + NST - 1;
+                        if (b < KB) issue_stage(cur, st, b);
+                        else if (piped) issue_stage(nx, st, b - KB);
+                        else issue_stage(cur, st, KB - 1);
+                        wait_vmem_le<(NST - 2) * NVM>();
+                        stage_barrier();
+                    }
+                });
             }
             // ... and, like the tail of an active wave, the early copies of the next
             // tile's block NST-1
             if (piped) {
 #pragma unroll
-                for (int t = 0; t < NFIRST; ++t) issue_copy(nx, t, stage_buf[NST - 1], NST - 1);
+                for (int t = 0; t < NFIRST; ++t) issue_copy(nx, t, stage(integral_constant<int, NST - 1>{}), NST - 1);
             }
         }
 
@@ -753,7 +782,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         // give every lane eight adjacent columns of one sub-tile, so a store
         // instruction writes 64 contiguous bytes per row in 16-byte pieces. ----
         if (cur.active) {
-            auto pack2 = [](float x, float y) -> uint32_t {
+            auto pack2 = [](float x, float y) DG_INLINE -> uint32_t {
                 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
                 const v2bf t = {(__bf16)x, (__bf16)y};
                 return __builtin_bit_cast(uint32_t, t);
@@ -864,8 +893,8 @@ static hipError_t occupancy_cfg(int* blocks) {
 
 static const KernelConfig kConfigs[] = {
     // dense
-    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 2, 1.00, true),
-    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 2, 0.90, true),
+    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 2, 1.00, false),
+    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 2, 0.90, false),
     DG_CFG(2, kDense, 128, 128, 2, 2, 16, 4, 0.55, false),
     DG_CFG(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false),
     DG_CFG(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true),
