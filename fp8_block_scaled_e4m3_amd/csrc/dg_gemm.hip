@@ -456,8 +456,9 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // previous K block (its scales are still held), so the matrix core never
     // waits for a promotion and a block boundary costs no pipeline drain.
     // LDS stages: block kb lives in stage kb % NST.  In each block the single
-    // workgroup barrier follows the first MFMA of the last column (step JB).  By
-    // then every wave has finished reading this block's stage, except for the
+    // workgroup barrier sits at step JB: two steps after the last read of this
+    // block's stage (16x16 sub-tiles; the first MFMA of the last column for 32x32).
+    // By then every wave has finished reading this block's stage, except for the
     // fragments already in registers, and has waited for its own copies of the
     // next block, so after the barrier
     //   * the next block's fragments are read while the last column's MFMAs run
@@ -468,7 +469,11 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // tile's first blocks: their copies, A scales and fragments arrive while this
     // tile finishes, so a tile boundary costs no pipeline refill either.
     constexpr int NJ = FN * FM;
-    constexpr int JB = (FN - 1) * FM;
+    // (the last read of this block's stage is the B fragment of the last column, at
+    // the first step of the column before it; an earlier barrier spreads the next
+    // block's first reads over more steps)
+    constexpr int EARLY = MF == 16 && FM > 2 ? FM - 2 : 0;
+    constexpr int JB = (FN - 1) * FM - EARLY;
     static_assert(FN >= 2, "the barrier sits in the last of at least two columns");
     // ring of in-flight partials: its position is a compile-time function of the
     // step because the block loop is unrolled by NST
