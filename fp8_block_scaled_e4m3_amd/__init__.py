@@ -273,10 +273,10 @@ def dg_plan_tiles(m: int, n: int, num_units: int, block_ms, block_ns, eff=None, 
 
 def dg_describe_launch(layout: int, m: int, n: int, k: int, num_groups: int = 1, num_cus: int = 0) -> dict:
     """The launch a call of these sizes would make (layout 0 dense, 1 contiguous, 2 masked)."""
-    out = (ctypes.c_int * 6)()
+    out = (ctypes.c_int * 7)()
     r = load_library().dg_describe_launch(layout, m, n, k, num_groups, num_cus, out)
     _check(r, "dg_describe_launch")
-    keys = ("block_m", "block_n", "waves_per_workgroup", "tiles", "grid", "config_id")
+    keys = ("block_m", "block_n", "waves_per_workgroup", "tiles", "grid", "config_id", "group_m")
     return dict(zip(keys, list(out)))
 
 

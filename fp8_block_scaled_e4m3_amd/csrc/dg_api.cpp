@@ -110,6 +110,30 @@ bool better(double cost, long waves, double best_cost, long best_waves) {
     return waves < best_waves;
 }
 
+// Row tiles per raster group (the tile order visits group_m row tiles across all
+// column tiles, then the next group).  With the XCD-aware hand-out each XCD gets
+// `chunk` consecutive tiles per round, i.e. a group_m x chunk/group_m block of the
+// output, whose A and B rows its L2 fetches once: prefer blocks that never straddle
+// two raster groups (group_m * tiles_n a multiple of chunk), then the block with
+// the fewest operand rows.  Without the XCD hand-out, 4.
+int raster_group_m(int tiles_m, int tiles_n, long chunk, int bm, int bn) {
+    if (chunk <= 0) return 4;
+    int best = 4;
+    long best_rows = 0;
+    bool best_whole = false;
+    for (int gm = 1; gm <= 16; gm *= 2) {
+        if (gm > tiles_m || chunk % gm) continue;
+        const bool whole = ((long)gm * tiles_n) % chunk == 0;
+        const long rows = (long)gm * bm + chunk / gm * bn;
+        if (best_rows == 0 || (whole && !best_whole) || (whole == best_whole && rows < best_rows)) {
+            best = gm;
+            best_rows = rows;
+            best_whole = whole;
+        }
+    }
+    return best;
+}
+
 // Pick among the compiled configurations of one layout.
 int choose_config(int layout, int m, int n, int num_groups, int num_units, const DeviceInfo* dev, int max_m_hint) {
     int count = 0;
@@ -166,12 +190,13 @@ int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_
         p.tiles_m = (int)ceil_div(p.rows, c.bm);
         p.num_tiles = p.tiles_m * p.tiles_n;
     }
-    p.group_m = group_m_override() > 0 ? group_m_override() : 4;
     long slots = (long)units * per_cu;
     long grid = p.num_tiles < slots ? p.num_tiles : slots;
     if (grid < 1) grid = 1;
     // keep whole rounds of 8 workgroups so the XCD hand-out stays a bijection
     p.xcd_remap = (grid % kXcds == 0) ? 1 : 0;
+    p.group_m = group_m_override() > 0 ? group_m_override()
+                                       : raster_group_m(p.tiles_m, p.tiles_n, p.xcd_remap ? grid / kXcds : 0, c.bm, c.bn);
 
     if (describe_out) {
         describe_out[0] = c.bm;
@@ -180,6 +205,7 @@ int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_
         describe_out[3] = p.num_tiles;
         describe_out[4] = (int)grid;
         describe_out[5] = c.id;
+        describe_out[6] = layout == dg::kMasked ? 0 : p.group_m;
         return DG_OK;
     }
     if (debug_enabled())

@@ -160,10 +160,12 @@ int dg_plan_tiles(int m, int n, int num_units, int blocks_per_unit,
                   const double* eff, int* out);
 
 /* Describe the kernel configuration a call with these sizes would launch, without
- * launching (layout 0 dense, 1 contiguous, 2 masked).  out[0..5] = block_m,
+ * launching (layout 0 dense, 1 contiguous, 2 masked).  out[0..6] = block_m,
  * block_n, waves per workgroup, tiles (upper bound for masked), persistent grid
- * size, config id.  num_cus <= 0 uses dg_get_num_cus().  Needs no device if
- * num_cus > 0 and assumes one resident workgroup per CU for the big shapes. */
+ * size, config id, row tiles per raster group of the tile order (0 for masked,
+ * whose order follows the groups); out must hold 7 ints.  num_cus <= 0 uses
+ * dg_get_num_cus().  Needs no device if num_cus > 0 and assumes one resident
+ * workgroup per CU for the big shapes. */
 int dg_describe_launch(int layout, int m, int n, int k, int num_groups, int num_cus, int* out);
 
 #ifdef __cplusplus

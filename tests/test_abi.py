@@ -122,8 +122,12 @@ def test_describe_launch_shapes():
     # planner's model: 448 tiles, the second round three quarters full
     d = dg.dg_describe_launch(0, 4096, 7168, 7168, 1, 256)
     assert (d["block_m"], d["block_n"], d["tiles"]) == (256, 256, 448) and d["grid"] == 256
+    # each XCD takes 32 consecutive tiles per round: 8 row tiles x 4 column tiles, and
+    # 8 x 28 = 224 tiles per raster group is a multiple of 32 (4 would straddle groups)
+    assert d["group_m"] == 8
     d = dg.dg_describe_launch(0, 256, 7168, 2048, 1, 256)
     assert (d["block_m"], d["block_n"], d["tiles"]) == (64, 112, 256)
+    assert d["group_m"] == 4                    # 4 row tiles x 8 column tiles of 64x112
     d = dg.dg_describe_launch(1, 33280, 4096, 7168, 8, 256)
     assert (d["block_m"], d["block_n"], d["tiles"]) == (256, 256, 130 * 16)
     d = dg.dg_describe_launch(2, 256, 4096, 7168, 16, 256)
