@@ -7,7 +7,7 @@ fp32 scales, BF16 out) with every input resident in HBM.  Prints ONE JSON line:
 whole-job FP8 TFLOPS, the kernel's roofline position (achieved TFLOP/s from HIP
 events around each launch on the launch stream, against the 5.0 PFLOP/s dense
 FP8 MFMA peak), the CPU oracle timed on a bounded sample of the same workload,
-and -- under "secondary" -- the other judged workloads (small-M dense, skewed
+and -- under "secondary" -- the other workloads (small-M dense, skewed
 contiguous MoE, masked decode) each timed the same way, HBM-bound ones with the
 caches flushed between launches.
 """
@@ -196,7 +196,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the GEMM library is single-GPU and this build runs no "
+        print("bench.py measures one GPU: the GEMM library is single-GPU and runs no "
               "multi-GPU configuration; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

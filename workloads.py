@@ -52,7 +52,7 @@ class Workload:
     extra: dict = field(default_factory=dict)
 
 
-# The five workloads the method is judged on: a small all-layout sanity shape,
+# The five workloads the library is measured on: a small all-layout sanity shape,
 # a prefill-like dense shape, an under-filled small-M dense shape, a skewed
 # contiguous MoE shape and a masked decode shape.
 WORKLOADS = {
