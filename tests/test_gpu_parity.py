@@ -340,3 +340,44 @@ def test_binding_reports_validation_errors():
         dg.dg_gemm_fp8_nt(a, sa, b, sb, d)
     assert e.value.status == dg.DG_ERR_UNSUPPORTED
     assert torch.count_nonzero(d).item() == 0
+
+
+# --------------------------------------------------------------------------- seeded sweep
+def test_seeded_random_shapes_planned(orc):
+    """A fixed-seed sweep of ragged shapes, group counts and CU caps through the planner
+    (whatever configuration, raster and variant it picks), each output compared in full."""
+    rng = np.random.default_rng(2024)
+    try:
+        for i in range(10):
+            m, n, k = int(rng.integers(1, 700)), 16 * int(rng.integers(1, 40)), 128 * int(rng.integers(1, 9))
+            cap = int(rng.choice([0, 3, 17, 64, 200]))
+            dg.dg_set_num_cus(cap)
+            say(f"sweep dense {m}x{n}x{k} cap {cap}", dg.dg_describe_launch(0, m, n, k, 1))
+            dd = W.make_dense(m, n, k, seed=100 + i)
+            out, full = run_dense(dd)
+            check_values(out, oracle_dense(orc, dd), f"sweep dense {m}x{n}x{k} cap {cap}")
+            assert np.all(full[:, n:] == W.SENTINEL_BF16)
+        for i in range(5):
+            counts = [int(c) for c in rng.integers(0, 400, size=int(rng.integers(1, 7)))]
+            n, k = 16 * int(rng.integers(1, 30)), 128 * int(rng.integers(1, 6))
+            cap = int(rng.choice([0, 5, 48]))
+            dg.dg_set_num_cus(cap)
+            cd = W.make_contiguous(counts, n=n, k=k, seed=200 + i)
+            say(f"sweep contiguous counts={counts} n={n} k={k} cap {cap}")
+            sentinel = np.full((cd["m_total"], n), W.SENTINEL_BF16, np.uint16)
+            ref = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], cd["m_indices"], d_init=sentinel)
+            valid = cd["m_indices"] >= 0
+            out = run_contiguous(cd)
+            check_values(out[valid], ref[valid], f"sweep contiguous {counts}")
+            assert np.all(out[~valid] == W.SENTINEL_BF16)
+        for i in range(5):
+            groups, max_m = int(rng.integers(1, 9)), int(rng.choice([64, 128, 200, 256]))
+            mm = [int(x) for x in rng.integers(0, max_m + 1, size=groups)]
+            n, k = 16 * int(rng.integers(1, 30)), 128 * int(rng.integers(1, 6))
+            cap = int(rng.choice([0, 7, 100]))
+            dg.dg_set_num_cus(cap)
+            md = W.make_masked(groups, max_m, n, k, seed=300 + i, masked_m=mm)
+            say(f"sweep masked masked_m={mm} max_m={max_m} n={n} k={k} cap {cap}")
+            check_masked(orc, md, run_masked(md))
+    finally:
+        dg.dg_set_num_cus(0)
