@@ -78,20 +78,60 @@ __device__ __forceinline__ float amax_of(const float* v, int n, float amax) {
     return amax;
 }
 
-// N codes of v / scale packed little-endian (4 -> one dword, 8 -> two)
+// Scales whose reciprocal is a normal number: the fast quotient below is exact there.
+__device__ __forceinline__ bool fast_scale(float scale) { return scale > 0x1p-125f && scale < 0x1p125f; }
+
+// x / scale correctly rounded, given r = RN(1/scale) with scale and r normal:
+// q = RN(x*r) is within one ulp of the quotient, the residual x - q*scale is exact
+// in a fused multiply-add, and one correction step rounds correctly (Markstein's
+// theorem for radix-2 division).  The quotient has the sign of x (scale > 0); the
+// copysign keeps it for x = -0, where the correction step would return +0.
+__device__ __forceinline__ float div_fast(float x, float scale, float r) {
+    const float q = x * r;
+    const float e = __builtin_fmaf(-q, scale, x);
+    return __builtin_copysignf(__builtin_fmaf(e, r, q), x);
+}
+
+// N codes of v / scale packed little-endian (4 -> one dword, 8 -> two).  Fast path
+// (every value of the wave finite or infinite but not NaN, the scale in range): the
+// quotient as above and gfx950's E4M3 convert, which rounds to nearest even with
+// subnormals and, for the magnitudes here (|q| <= 448 up to one rounding), agrees
+// with e4m3_code.  Otherwise each code is computed in software with an IEEE division.
 template <int N>
-__device__ __forceinline__ void store_codes(uint8_t* dst, const float* v, float scale) {
+__device__ __forceinline__ void store_codes(uint8_t* dst, const float* v, float scale, bool fast) {
     uint32_t w[N / 4];
+    if (fast) {
+        const float r = 1.0f / scale;
 #pragma unroll
-    for (int d = 0; d < N / 4; ++d) {
-        uint32_t c = 0;
+        for (int d = 0; d < N / 4; ++d) {
+            int c = __builtin_amdgcn_cvt_pk_fp8_f32(div_fast(v[4 * d], scale, r), div_fast(v[4 * d + 1], scale, r), 0,
+                                                    false);
+            c = __builtin_amdgcn_cvt_pk_fp8_f32(div_fast(v[4 * d + 2], scale, r), div_fast(v[4 * d + 3], scale, r), c,
+                                                true);
+            w[d] = (uint32_t)c;
+        }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) c |= e4m3_code(v[4 * d + e] / scale) << (8 * e);
-        w[d] = c;
+        for (int d = 0; d < N / 4; ++d) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c |= e4m3_code(v[4 * d + e] / scale) << (8 * e);
+            w[d] = c;
+        }
     }
     if constexpr (N == 4) *(uint32_t*)dst = w[0];
     else *(uint2*)dst = uint2{w[0], w[1]};
 }
+
+// true when any of the n values is a NaN
+__device__ __forceinline__ bool any_nan(const float* v, int n) {
+    bool r = false;
+    for (int i = 0; i < n; ++i) r |= v[i] != v[i];
+    return r;
+}
+
+// one decision for the whole wave, so the paths never diverge inside it
+__device__ __forceinline__ bool wave_all(bool b) { return __ballot(!b) == 0; }
 
 // 1x128: a 128-element row block is read by L = 128/N lanes with one 16-byte load
 // each (the block's bytes are contiguous, so every load instruction is coalesced).
@@ -131,7 +171,8 @@ quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, uin
         }
         const float scale = amax == 0.f ? 1.f : amax / kE4M3Max;
         const unsigned row = g / (unsigned)kblocks, kb = g - row * (unsigned)kblocks;
-        store_codes<N>(q + (long)row * ldq + kb * kQBlock + lg * N, v[r], scale);
+        const bool fast = wave_all(fast_scale(scale) && !any_nan(v[r], N));
+        store_codes<N>(q + (long)row * ldq + kb * kQBlock + lg * N, v[r], scale, fast);
         if (lg == 0) sa[(long)kb * ld_sa + row] = scale;
     }
 }
@@ -174,10 +215,14 @@ quant_128x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, u
     for (int w = 1; w < 4; ++w) amax = s_amax[w] > amax ? s_amax[w] : amax;
     const float scale = amax == 0.f ? 1.f : amax / kE4M3Max;
     if (t == 0) sb[(long)rb * kblocks + kb] = scale;
+    bool nan = false;
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) nan |= any_nan(v[i], N);
+    const bool fast = wave_all(fast_scale(scale) && !nan);
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
         const int row = r0 + i * RPP;
-        if (row < rows) store_codes<N>(q + (long)row * ldq + c0, v[i], scale);
+        if (row < rows) store_codes<N>(q + (long)row * ldq + c0, v[i], scale, fast);
     }
 }
 

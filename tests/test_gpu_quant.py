@@ -35,6 +35,8 @@ def specials(x):
     x[5, k - 1] = np.inf                      # amax inf: others -> +-0, inf -> NaN code
     x[6, :128] = np.float32(448.0) * np.linspace(-1, 1, 128, dtype=np.float32)
     x[7, :] = np.float32(2.0) ** ((np.arange(k) % 48) - 30).astype(np.float32)   # wide magnitude range
+    if x.shape[0] > 8:
+        x[8, :128] = np.float32(1e-40) * np.arange(-64, 64, dtype=np.float32)    # fp32-subnormal block: tiny scale
     return x
 
 
@@ -84,6 +86,39 @@ def test_quant_1x128_bit_exact(orc, rows, k, dtype):
     assert np.array_equal(q, rq), f"{np.sum(q != rq)} codes differ"
     assert same_bits(sa[:, :rows], rsa)
     assert np.all(sa[:, rows:] == -1.0)                     # padding columns untouched
+
+
+def e4m3_rounding_grid():
+    """fp32 values at and around every E4M3 rounding decision in [-448, 448]: each
+    representable value, each tie between neighbours and the fp32 values one ulp to
+    either side of it, for normal and subnormal codes, plus values that round to 0."""
+    vals = []
+    for e in range(-9, 9):                       # E4M3 exponents (normal from -6, spacing 2^(e-3))
+        for m in range(16):
+            for frac in (0.0, 0.5):
+                v = np.float32(2.0 ** e * (1 + (m + frac) / 8)) if e >= -6 else np.float32((m + frac) * 2.0 ** -9)
+                vals += [v, np.nextafter(v, np.float32(0)), np.nextafter(v, np.float32(1e9))]
+    vals += [np.float32(2.0 ** -10), np.float32(2.0 ** -11), np.float32(1e-20), np.float32(0.0)]
+    v = np.array(vals, np.float32)
+    v = v[np.abs(v) <= 448]
+    return np.concatenate([v, -v])
+
+
+def test_quant_conversion_grid_bit_exact(orc):
+    """With 448 in every block the scale is exactly 1, so the codes are the E4M3
+    conversion itself: every rounding decision of the format, both signs, compared
+    with the oracle's encoder."""
+    grid = e4m3_rounding_grid()
+    per = 127
+    nblk = -(-grid.size // per)
+    nblk += -nblk % 4                             # four blocks per row
+    body = np.resize(grid, nblk * per).reshape(nblk, per)
+    x = np.concatenate([np.full((nblk, 1), 448.0, np.float32), body], axis=1).reshape(-1, 128 * 4)
+    rows = x.shape[0]
+    q, sa = gpu_1x128(to_dev(x), rows, x.shape[1])
+    rq, rsa = orc.quantize_rows_1x128(x)
+    assert np.all(sa[:, :rows] == 1.0)
+    assert np.array_equal(q, rq), f"{np.sum(q != rq)} codes differ"
 
 
 @pytest.mark.parametrize("rows,k", [(128, 128), (200, 384), (1, 256), (385, 512)])
