@@ -10,13 +10,15 @@ computes, and which passage of the pages each step follows, is documented at
 the top of ``oracle.c``:
 
 * ``e4m3_decode_table`` -- OCP E4M3FN value of every byte (hnwysp.cn blog
-  section 4.1 fixes the +-448 range);
+  section 4.1 fixes the +-448 range); ``e5m2_decode_table`` -- OCP E5M2, the
+  other operand format the blog lists (section 2.3);
 * ``e4m3_encode`` / ``bf16_encode`` -- round-to-nearest-even encoders;
 * ``quantize_rows_1x128`` / ``quantize_blocks_128x128`` -- the input cast with
   per-block scales (the README's usage paragraph leaves the cast to a prior
   kernel; the granularity is the DeepSeek-V3 fine-grained scheme);
 * ``gemm_fp8_nt`` / ``m_grouped_contiguous`` / ``m_grouped_masked`` -- the three
-  layouts of the README ("normal", "contiguous", "masked" paragraphs).
+  layouts of the README ("normal", "contiguous", "masked" paragraphs); the dense
+  GEMM also takes each operand's format (E4M3 or E5M2).
 """
 from __future__ import annotations
 
@@ -66,6 +68,12 @@ def _load():
     lib.orc_bf16_encode.restype = ctypes.c_uint16
     lib.orc_block_dot.argtypes = [P, P, I]
     lib.orc_block_dot.restype = ctypes.c_double
+    lib.orc_e5m2_decode_table.argtypes = [P]
+    lib.orc_e5m2_decode_table.restype = None
+    lib.orc_block_dot_fmt.argtypes = [P, P, I, I, I]
+    lib.orc_block_dot_fmt.restype = ctypes.c_double
+    lib.orc_gemm_fp8_nt_fmt.argtypes = [P, L, P, L, P, L, P, P, L, P, I, I, I, I, I, I]
+    lib.orc_gemm_fp8_nt_fmt.restype = I
     lib.orc_quantize_rows_1x128.argtypes = [P, L, I, I, P, L, P, L]
     lib.orc_quantize_rows_1x128.restype = None
     lib.orc_quantize_blocks_128x128.argtypes = [P, L, I, I, P, L, P]
@@ -108,6 +116,15 @@ def e4m3_decode_table() -> np.ndarray:
     return out
 
 
+def e5m2_decode_table() -> np.ndarray:
+    out = np.empty(256, dtype=np.float64)
+    _load().orc_e5m2_decode_table(_ptr(out))
+    return out
+
+
+FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
 def e4m3_encode(x: float) -> int:
     return int(_load().orc_e4m3_encode(float(x)))
 
@@ -120,6 +137,13 @@ def block_dot(a, b) -> float:
     a, b = _u8(a), _u8(b)
     assert a.shape == b.shape and a.ndim == 1
     return float(_load().orc_block_dot(_ptr(a), _ptr(b), int(a.size)))
+
+
+def block_dot_fmt(a, b, a_fmt="e4m3", b_fmt="e4m3") -> float:
+    """Block dot product with each operand in its own format, summed exactly."""
+    a, b = _u8(a), _u8(b)
+    assert a.shape == b.shape and a.ndim == 1
+    return float(_load().orc_block_dot_fmt(_ptr(a), _ptr(b), int(a.size), FORMATS[a_fmt], FORMATS[b_fmt]))
 
 
 def quantize_rows_1x128(x):
@@ -143,10 +167,10 @@ def quantize_blocks_128x128(x):
     return q, sb
 
 
-def gemm_fp8_nt(a, sa, b, sb, *, d_init=None, want_acc=False, nthreads=0):
-    """Dense NT GEMM.  a: E4M3 [m, k]; sa: fp32 [Kb, ld_sa>=m] (MN-major);
-    b: E4M3 [n, k]; sb: fp32 [ceil(n/128), Kb].  Returns BF16 bits uint16 [m, n]
-    (and the fp64 accumulator when ``want_acc``)."""
+def gemm_fp8_nt(a, sa, b, sb, *, d_init=None, want_acc=False, nthreads=0, a_fmt="e4m3", b_fmt="e4m3"):
+    """Dense NT GEMM.  a: FP8 [m, k]; sa: fp32 [Kb, ld_sa>=m] (MN-major);
+    b: FP8 [n, k]; sb: fp32 [ceil(n/128), Kb]; each operand E4M3 or E5M2.  Returns
+    BF16 bits uint16 [m, n] (and the fp64 accumulator when ``want_acc``)."""
     a, b, sa, sb = _u8(a), _u8(b), _f32(sa), _f32(sb)
     m, k = a.shape
     n = b.shape[0]
@@ -154,8 +178,13 @@ def gemm_fp8_nt(a, sa, b, sb, *, d_init=None, want_acc=False, nthreads=0):
     assert sb.shape == (-(-n // KBLOCK), -(-k // KBLOCK))
     d = np.zeros((m, n), np.uint16) if d_init is None else np.array(d_init, np.uint16, copy=True)
     acc = np.full((m, n), np.nan) if want_acc else None
-    _load().orc_gemm_fp8_nt(_ptr(a), k, _ptr(sa), sa.shape[1], _ptr(b), k, _ptr(sb),
-                            _ptr(d), n, _ptr(acc), m, n, k, int(nthreads))
+    if a_fmt == "e4m3" and b_fmt == "e4m3":
+        _load().orc_gemm_fp8_nt(_ptr(a), k, _ptr(sa), sa.shape[1], _ptr(b), k, _ptr(sb),
+                                _ptr(d), n, _ptr(acc), m, n, k, int(nthreads))
+    else:
+        _load().orc_gemm_fp8_nt_fmt(_ptr(a), k, _ptr(sa), sa.shape[1], _ptr(b), k, _ptr(sb),
+                                    _ptr(d), n, _ptr(acc), m, n, k, FORMATS[a_fmt], FORMATS[b_fmt],
+                                    int(nthreads))
     return (d, acc) if want_acc else d
 
 

@@ -1,6 +1,7 @@
 /*
  * oracle.c -- plain, slow, CPU-only reference for the fine-grained-scaled
- * FP8 E4M3 "NT" GEMM (dense, M-grouped contiguous, M-grouped masked).
+ * FP8 E4M3 "NT" GEMM (dense, M-grouped contiguous, M-grouped masked), and for
+ * the dense GEMM with E5M2 operands.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the oracle that the HIP library is
  * checked against.  Only the test suite, the smoke check and the bench's CPU
@@ -30,14 +31,20 @@
  *    P_kb the exact dot product over the K block, evaluated here in fp64 and
  *    rounded once to BF16 (round-to-nearest-even);
  *  - a K that is not a multiple of 128 ends in a short last block whose scale
- *    covers only the remaining columns.
+ *    covers only the remaining columns;
+ *  - E5M2 (hnwysp.cn blog section 2.3 lists it beside E4M3; the README's
+ *    functions are FP8 x FP8) is the OCP E5M2 encoding (max 57344, subnormals,
+ *    infinities, NaN = S.11111.{01,10,11}); either operand may use it, the
+ *    scales and the promotion are unchanged.
  *
  * Why fp64 is (nearly) exact here: every E4M3 value is an integer multiple of
  * 2^-9 with magnitude below 2^18 units, so every product is an integer multiple
  * of 2^-18 below 2^36 units and a 128-term block sum stays below 2^43 units --
  * exact in a 53-bit significand in any summation order.  The product of two
  * fp32 scales is exact in fp64.  The only roundings are one multiply and one
- * add per K block (relative 2^-53) and the final BF16 rounding.
+ * add per K block (relative 2^-53) and the final BF16 rounding.  With an E5M2
+ * operand the block sum can need more than 53 bits; it is formed exactly in
+ * 128-bit integers and rounded once to fp64.
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -66,17 +73,52 @@ static double e4m3_value(unsigned b)
     return s ? -mag : mag;
 }
 
-static double DEC[256];
+/* ------------------------------------------------------------------------- */
+/* E5M2 (OCP), the second FP8 format the hnwysp.cn blog lists for operands   */
+/* (section 2.3).  Byte layout s.eeeee.ff, exponent bias 15.                 */
+/*   e == 31: f == 0 -> +-infinity, otherwise NaN                            */
+/*   e == 0          -> subnormal (-1)^s * f * 2^-16                         */
+/*   otherwise       -> (-1)^s * (1 + f/4) * 2^(e-15) = (4+f) * 2^(e-17)     */
+/* ------------------------------------------------------------------------- */
+static double e5m2_value(unsigned b)
+{
+    unsigned s = (b >> 7) & 1u, e = (b >> 2) & 31u, f = b & 3u;
+    double mag;
+    if (e == 31u) mag = f == 0u ? INFINITY : NAN;
+    else if (e == 0u) mag = ldexp((double)f, -16);
+    else mag = ldexp((double)(4u + f), (int)e - 17);
+    return s ? -mag : mag;
+}
+
+/* Every finite value of a format is an integer multiple of its smallest
+ * subnormal, 2^-SHIFT: MANT[b] = value * 2^SHIFT (E4M3: |MANT| <= 229376,
+ * E5M2: |MANT| <= 57344 * 2^16 < 2^32). */
+static const int FMT_SHIFT[2] = {9, 16};
+
+static double DEC[256];          /* E4M3 */
+static double DEC5[256];         /* E5M2 */
+static int64_t MANT[2][256];
 static pthread_once_t dec_once = PTHREAD_ONCE_INIT;
 static void dec_init(void)
 {
-    for (unsigned b = 0; b < 256u; ++b) DEC[b] = e4m3_value(b);
+    for (unsigned b = 0; b < 256u; ++b) {
+        DEC[b] = e4m3_value(b);
+        DEC5[b] = e5m2_value(b);
+        MANT[0][b] = isfinite(DEC[b]) ? (int64_t)ldexp(DEC[b], FMT_SHIFT[0]) : 0;
+        MANT[1][b] = isfinite(DEC5[b]) ? (int64_t)ldexp(DEC5[b], FMT_SHIFT[1]) : 0;
+    }
 }
 
 void orc_e4m3_decode_table(double out[256])
 {
     pthread_once(&dec_once, dec_init);
     memcpy(out, DEC, sizeof(DEC));
+}
+
+void orc_e5m2_decode_table(double out[256])
+{
+    pthread_once(&dec_once, dec_init);
+    memcpy(out, DEC5, sizeof(DEC5));
 }
 
 /* ------------------------------------------------------------------------- */
@@ -209,16 +251,42 @@ double orc_block_dot(const uint8_t* a, const uint8_t* b, int len)
     return p;
 }
 
+/* The same block dot product with each operand in its own format (0 = E4M3,
+ * 1 = E5M2).  With E5M2 a 128-term sum no longer fits a 53-bit significand, so
+ * the products of the integer forms are summed exactly in 128-bit integers and
+ * the sum is rounded once to fp64 (then scaled by a power of two, exact).  A
+ * block holding an infinity or a NaN is summed in fp64 instead, which gives
+ * the IEEE result. */
+double orc_block_dot_fmt(const uint8_t* a, const uint8_t* b, int len, int fa, int fb)
+{
+    const double* da;
+    const double* db;
+    __int128 sum = 0;
+    int finite = 1;
+    pthread_once(&dec_once, dec_init);
+    da = fa ? DEC5 : DEC;
+    db = fb ? DEC5 : DEC;
+    for (int t = 0; t < len; ++t) finite &= isfinite(da[a[t]]) && isfinite(db[b[t]]);
+    if (!finite) {
+        double p = 0.0;
+        for (int t = 0; t < len; ++t) p += da[a[t]] * db[b[t]];
+        return p;
+    }
+    for (int t = 0; t < len; ++t) sum += (__int128)MANT[fa][a[t]] * (__int128)MANT[fb][b[t]];
+    return ldexp((double)sum, -(FMT_SHIFT[fa] + FMT_SHIFT[fb]));
+}
+
 /* One output element of the method (all layouts reduce to this):           */
 /*   acc = sum_kb (sA[kb] * sB[kb]) * P_kb,  kb ascending, fp64.             */
 static double scaled_row_col(const uint8_t* arow, const float* sa_col, long ld_sa,
-                             const uint8_t* brow, const float* sb_row, int k)
+                             const uint8_t* brow, const float* sb_row, int k, int fa, int fb)
 {
     int kbn = (k + ORC_KBLOCK - 1) / ORC_KBLOCK;
     double acc = 0.0;
     for (int kb = 0; kb < kbn; ++kb) {
         int k0 = kb * ORC_KBLOCK, len = k - k0 < ORC_KBLOCK ? k - k0 : ORC_KBLOCK;
-        double p = orc_block_dot(arow + k0, brow + k0, len);
+        double p = (fa || fb) ? orc_block_dot_fmt(arow + k0, brow + k0, len, fa, fb)
+                              : orc_block_dot(arow + k0, brow + k0, len);
         double s = (double)sa_col[(long)kb * ld_sa] * (double)sb_row[kb];
         acc += s * p;
     }
@@ -241,6 +309,7 @@ typedef struct {
     const int* masked_m;      /* masked */
     int max_m;                /* masked: rows per group */
     double* acc_out;          /* optional fp64 result (same indexing as d), may be NULL */
+    int a_fmt, b_fmt;         /* operand formats: 0 E4M3, 1 E5M2 */
     /* work split */
     int nthreads, tid;
 } orc_job;
@@ -275,7 +344,7 @@ static void do_row(const orc_job* J, long row)
     sbg = J->sb + (long)g * J->sb_group_stride;
     for (int j = 0; j < J->n; ++j) {
         double acc = scaled_row_col(arow, sa_col, J->ld_sa, bg + (long)j * J->ldb,
-                                    sbg + (long)(j / ORC_KBLOCK) * kbn, J->k);
+                                    sbg + (long)(j / ORC_KBLOCK) * kbn, J->k, J->a_fmt, J->b_fmt);
         J->d[row * J->ldd + j] = orc_bf16_encode(acc);
         if (J->acc_out) J->acc_out[row * J->ldd + j] = acc;
     }
@@ -333,6 +402,22 @@ int orc_gemm_fp8_nt(const uint8_t* a, long lda, const float* sa, long ld_sa,
     J.a = a; J.lda = lda; J.sa = sa; J.ld_sa = ld_sa;
     J.b = b; J.ldb = ldb; J.sb = sb; J.d = d; J.ldd = ldd; J.acc_out = acc_out;
     J.m = m; J.n = n; J.k = k; J.layout = 0;
+    return run_rows(J, nthreads);
+}
+
+/* Dense NT GEMM with each operand in its own FP8 format (0 E4M3, 1 E5M2);
+ * otherwise as orc_gemm_fp8_nt, which it equals for two E4M3 operands. */
+int orc_gemm_fp8_nt_fmt(const uint8_t* a, long lda, const float* sa, long ld_sa,
+                        const uint8_t* b, long ldb, const float* sb,
+                        uint16_t* d, long ldd, double* acc_out,
+                        int m, int n, int k, int a_fmt, int b_fmt, int nthreads)
+{
+    orc_job J;
+    memset(&J, 0, sizeof(J));
+    J.a = a; J.lda = lda; J.sa = sa; J.ld_sa = ld_sa;
+    J.b = b; J.ldb = ldb; J.sb = sb; J.d = d; J.ldd = ldd; J.acc_out = acc_out;
+    J.m = m; J.n = n; J.k = k; J.layout = 0;
+    J.a_fmt = a_fmt != 0; J.b_fmt = b_fmt != 0;
     return run_rows(J, nthreads);
 }
 

@@ -173,6 +173,94 @@ def test_block_dot_equals_int64_sum(orc):
         assert orc.block_dot(a[perm], b[perm]) == got       # order never matters
 
 
+# --------------------------------------------------------------------------- E5M2 (second operand format)
+def torch_e5m2_values():
+    """float64 value of every E5M2 byte, decoded by torch (independent of the oracle)."""
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e5m2) \
+        .to(torch.float64).numpy()
+
+
+def test_e5m2_table_closed_forms(orc):
+    dec = orc.e5m2_decode_table()
+    assert dec[0x00] == 0.0 and math.copysign(1.0, dec[0x80]) == -1.0
+    assert dec[0x01] == 2.0 ** -16 and dec[0x03] == 3 * 2.0 ** -16       # subnormals
+    assert dec[0x04] == 2.0 ** -14                                          # smallest normal
+    assert dec[0x3C] == 1.0 and dec[0x3D] == 1.25 and dec[0x40] == 2.0
+    assert dec[0x7B] == 57344.0                                             # largest finite
+    assert dec[0x7C] == math.inf and dec[0xFC] == -math.inf
+    assert all(math.isnan(dec[b]) for b in (0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF))
+    for b in range(0x7C):
+        assert dec[b | 0x80] == -dec[b] or (b == 0 and dec[0x80] == 0.0)
+        if b:
+            assert dec[b] > dec[b - 1]
+
+
+def test_e5m2_table_matches_torch(orc):
+    dec, ref = orc.e5m2_decode_table(), torch_e5m2_values()
+    assert np.array_equal(np.isnan(dec), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(dec[ok], ref[ok])
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e4m3")])
+def test_block_dot_fmt_is_exact_sum_rounded_once(orc, fa, fb):
+    """The block sum with E5M2 operands needs up to ~70 bits: it must equal the exact
+    rational sum rounded once to fp64 (Python's Fraction -> float rounds correctly),
+    also for blocks of the largest values where an fp64 running sum would round."""
+    va = torch_e5m2_values() if fa == "e5m2" else torch_e4m3_values()
+    vb = torch_e5m2_values() if fb == "e5m2" else torch_e4m3_values()
+    fin_a = np.array([b for b in range(256) if np.isfinite(va[b])], np.uint8)
+    fin_b = np.array([b for b in range(256) if np.isfinite(vb[b])], np.uint8)
+    rng = np.random.default_rng(6)
+    for trial in range(150):
+        a, b = rng.choice(fin_a, 128), rng.choice(fin_b, 128)
+        if trial % 3 == 0:                          # extremes: the largest and smallest magnitudes
+            a[::2] = fin_a[np.argmax(np.abs(va[fin_a]))]
+            b[1::2] = fin_b[np.argmin(np.where(vb[fin_b] == 0, np.inf, np.abs(vb[fin_b])))]
+        exact = sum(Fraction(float(va[x])) * Fraction(float(vb[y])) for x, y in zip(a, b))
+        assert orc.block_dot_fmt(a, b, fa, fb) == float(exact)
+        if fa == fb == "e4m3":
+            assert orc.block_dot_fmt(a, b) == orc.block_dot(a, b)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2")])
+def test_gemm_fmt_equals_exact_rational(orc, fa, fb):
+    """The dense GEMM with E5M2 operands against exact rational brute force rounded once
+    to BF16 (several K blocks, a short last block, two B-scale blocks)."""
+    m, n, k = 3, 133, 300
+    rng = np.random.default_rng(7 + len(fa + fb))
+    va = torch_e5m2_values() if fa == "e5m2" else torch_e4m3_values()
+    vb = torch_e5m2_values() if fb == "e5m2" else torch_e4m3_values()
+    fin_a = np.array([b for b in range(256) if np.isfinite(va[b])], np.uint8)
+    fin_b = np.array([b for b in range(256) if np.isfinite(vb[b])], np.uint8)
+    a, b = rng.choice(fin_a, (m, k)), rng.choice(fin_b, (n, k))
+    kb, nb = -(-k // 128), -(-n // 128)
+    sa = (rng.uniform(0.5, 2, (kb, m)) * 2.0 ** rng.integers(-12, 0, (kb, m))).astype(np.float32)
+    sb = (rng.uniform(0.5, 2, (nb, kb)) * 2.0 ** rng.integers(-12, 0, (nb, kb))).astype(np.float32)
+    d = orc.gemm_fp8_nt(a, sa, b, sb, a_fmt=fa, b_fmt=fb)
+    for i in range(m):
+        for j in range(0, n, 7):
+            tot = Fraction(0)
+            for blk in range(kb):
+                ks = range(blk * 128, min(k, blk * 128 + 128))
+                p = sum(Fraction(float(va[a[i, t]])) * Fraction(float(vb[b[j, t]])) for t in ks)
+                tot += Fraction(float(sa[blk, i])) * Fraction(float(sb[j // 128, blk])) * p
+            assert d[i, j] == _exact_bf16(tot), (i, j)
+
+
+def test_gemm_fmt_e4m3_matches_plain_path(orc):
+    rng = np.random.default_rng(8)
+    a, b = _rand_fp8(rng, (5, 256)), _rand_fp8(rng, (40, 256))
+    sa = rng.uniform(0.5, 2, (2, 8)).astype(np.float32)
+    sb = rng.uniform(0.5, 2, (1, 2)).astype(np.float32)
+    plain = orc.gemm_fp8_nt(a, sa, b, sb)
+    lib = orc._load()
+    d = np.zeros((5, 40), np.uint16)
+    lib.orc_gemm_fp8_nt_fmt(orc._ptr(a), 256, orc._ptr(sa), 8, orc._ptr(b), 256, orc._ptr(sb),
+                            orc._ptr(d), 40, None, 5, 40, 256, 0, 0, 1)
+    assert np.array_equal(d, plain)
+
+
 # --------------------------------------------------------------------------- whole GEMM
 def _exact_bf16(x: Fraction) -> int:
     """Round an exact rational to BF16 (RNE), written with rationals only."""
