@@ -58,6 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_get_num_cus.restype = I
     lib.dg_gemm_fp8_nt.argtypes = [P, L, P, L, P, L, P, P, L, I, I, I, P]
     lib.dg_gemm_fp8_nt.restype = I
+    lib.dg_gemm_fp8_nt_fmt.argtypes = [P, L, P, L, P, L, P, P, L, I, I, I, I, I, P]
+    lib.dg_gemm_fp8_nt_fmt.restype = I
     lib.dg_m_grouped_gemm_fp8_contiguous.argtypes = [P, P, L, P, P, P, P, I, I, I, I, P]
     lib.dg_m_grouped_gemm_fp8_contiguous.restype = I
     lib.dg_m_grouped_gemm_fp8_masked.argtypes = [P, P, L, P, P, P, P, I, I, I, I, P]
@@ -117,6 +119,29 @@ def _fp8_types():
     return (torch.float8_e4m3fn, torch.uint8)
 
 
+def _fp8_any_types():
+    import torch
+    return (torch.float8_e4m3fn, torch.float8_e5m2, torch.uint8)
+
+
+DG_FMT_E4M3, DG_FMT_E5M2 = 0, 1
+_FMT_NAMES = {"e4m3": DG_FMT_E4M3, "e5m2": DG_FMT_E5M2}
+
+
+def _fmt_of(t, given):
+    """Operand format: a float8 dtype carries it (float8_e5m2 -> E5M2, float8_e4m3fn ->
+    E4M3); for uint8 bytes ``given`` ("e4m3" / "e5m2") decides, E4M3 when None."""
+    import torch
+    from_dtype = {torch.float8_e5m2: DG_FMT_E5M2, torch.float8_e4m3fn: DG_FMT_E4M3}.get(t.dtype)
+    if given is None:
+        return DG_FMT_E4M3 if from_dtype is None else from_dtype
+    if given not in _FMT_NAMES:
+        raise ValueError(f"unknown FP8 format {given!r}")
+    if from_dtype is not None and from_dtype != _FMT_NAMES[given]:
+        raise ValueError(f"format {given!r} does not match dtype {t.dtype}")
+    return _FMT_NAMES[given]
+
+
 def _f32():
     import torch
     return (torch.float32,)
@@ -143,22 +168,31 @@ def dg_get_num_cus() -> int:
 
 
 def dg_gemm_fp8_nt(a, sa, b, sb, d, stream=None) -> None:
-    """D[m, n] = bf16(sum_kb sA[kb, m] * sB[n // 128, kb] * A[m, kb-block] . B[n, kb-block])."""
+    """D[m, n] = bf16(sum_kb sA[kb, m] * sB[n // 128, kb] * A[m, kb-block] . B[n, kb-block]).
+    E4M3 operands; a tensor of dtype float8_e5m2 is taken as E5M2 (see dg_gemm_fp8_nt_fmt)."""
+    dg_gemm_fp8_nt_fmt(a, sa, b, sb, d, None, None, stream)
+
+
+def dg_gemm_fp8_nt_fmt(a, sa, b, sb, d, a_fmt=None, b_fmt=None, stream=None) -> None:
+    """The dense GEMM with each operand E4M3 or E5M2 ("e4m3" / "e5m2"; float8 tensors
+    carry their format in the dtype, uint8 bytes default to E4M3)."""
     m, k = a.shape
     n = b.shape[0]
-    pa = _dev(a, "a", _fp8_types(), 2)
+    pa = _dev(a, "a", _fp8_any_types(), 2)
     psa = _dev(sa, "sa", _f32(), 2)
-    pb = _dev(b, "b", _fp8_types(), 2)
+    pb = _dev(b, "b", _fp8_any_types(), 2)
     psb = _dev(sb, "sb", _f32(), 2)
     pd = _dev(d, "d", _bf16_types(), 2)
+    fa, fb = _fmt_of(a, a_fmt), _fmt_of(b, b_fmt)
     if b.shape[1] != k or tuple(d.shape) != (m, n):
         raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, d {tuple(d.shape)}")
     if sa.shape[0] != -(-k // 128) or sb.shape[1] != -(-k // 128) or sb.shape[0] != -(-n // 128):
         raise ValueError(f"scale shape mismatch: sa {tuple(sa.shape)}, sb {tuple(sb.shape)}")
     if not sb.is_contiguous():
         raise ValueError("sb must be contiguous")
-    _check(load_library().dg_gemm_fp8_nt(pa, a.stride(0), psa, sa.stride(0), pb, b.stride(0), psb,
-                                         pd, d.stride(0), m, n, k, _stream(stream)), "dg_gemm_fp8_nt")
+    _check(load_library().dg_gemm_fp8_nt_fmt(pa, a.stride(0), psa, sa.stride(0), pb, b.stride(0), psb,
+                                             pd, d.stride(0), m, n, k, fa, fb, _stream(stream)),
+           "dg_gemm_fp8_nt_fmt")
 
 
 def dg_m_grouped_gemm_fp8_contiguous(a, sa, b, sb, d, m_indices, stream=None) -> None:
@@ -250,10 +284,11 @@ def dg_set_kernel_config(config_id: int) -> None:
 
 
 def dg_kernel_config_info() -> list:
-    """All compiled kernel configurations as dicts (id, layout, block_m, block_n, waves)."""
-    out, res, i = (ctypes.c_int * 5)(), [], 0
+    """All compiled kernel configurations as dicts (id, layout, block_m, block_n, waves,
+    all_formats: whether E5M2 operands run in it)."""
+    out, res, i = (ctypes.c_int * 6)(), [], 0
     while load_library().dg_kernel_config_info(i, out) == DG_OK:
-        res.append(dict(zip(("id", "layout", "block_m", "block_n", "waves"), list(out))))
+        res.append(dict(zip(("id", "layout", "block_m", "block_n", "waves", "all_formats"), list(out))))
         i += 1
     return res
 
@@ -283,6 +318,6 @@ def dg_describe_launch(layout: int, m: int, n: int, k: int, num_groups: int = 1,
 __all__ = [
     "DGError", "load_library", "status_string", "dg_status_string",
     "dg_get_m_alignment", "dg_set_num_cus", "dg_get_num_cus",
-    "dg_gemm_fp8_nt", "dg_m_grouped_gemm_fp8_contiguous", "dg_m_grouped_gemm_fp8_masked",
+    "dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "DG_FMT_E4M3", "DG_FMT_E5M2", "dg_m_grouped_gemm_fp8_contiguous", "dg_m_grouped_gemm_fp8_masked",
     "dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_set_kernel_config", "dg_kernel_config_info", "dg_plan_tiles", "dg_describe_launch",
 ]

@@ -135,17 +135,18 @@ int raster_group_m(int tiles_m, int tiles_n, long chunk, int bm, int bn) {
 }
 
 // Pick among the compiled configurations of one layout.
-int choose_config(int layout, int m, int n, int num_groups, int num_units, const DeviceInfo* dev, int max_m_hint) {
+int choose_config(int layout, int m, int n, int num_groups, int fmt, int num_units, const DeviceInfo* dev,
+                  int max_m_hint) {
     int count = 0;
     const KernelConfig* cfgs = dg::kernel_configs(&count);
     const int forced = g_forced_cfg[layout].load();
-    if (forced >= 0 && forced < count) return forced;
+    if (forced >= 0 && forced < count) return (fmt == 0 || cfgs[forced].all_formats) ? forced : -1;
     int best = -1;
     double best_cost = 0.0;
     long best_waves = 0;
     for (int i = 0; i < count; ++i) {
         const KernelConfig& c = cfgs[i];
-        if (c.layout != layout) continue;
+        if (c.layout != layout || (fmt != 0 && !c.all_formats)) continue;
         // Masked: the whole capacity in one row block when it fits (B is then streamed
         // once per group), else the largest block; among those the cost model below on
         // the upper bound of the tile count (every group full), so that a CU cap that
@@ -177,7 +178,7 @@ int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_
     }
     int count = 0;
     const KernelConfig* cfgs = dg::kernel_configs(&count);
-    const int ci = choose_config(layout, m_for_plan, p.n, p.num_groups, units, dev, max_m_hint);
+    const int ci = choose_config(layout, m_for_plan, p.n, p.num_groups, p.fmt, units, dev, max_m_hint);
     if (ci < 0) return DG_ERR_UNSUPPORTED;
     const KernelConfig& c = cfgs[ci];
     const int per_cu = dev ? dev->occ[ci] : 1;
@@ -324,6 +325,7 @@ int dg_kernel_config_info(int index, int* out) {
     out[2] = cfgs[index].bm;
     out[3] = cfgs[index].bn;
     out[4] = cfgs[index].wm * cfgs[index].wn;
+    out[5] = cfgs[index].all_formats ? 1 : 0;
     return DG_OK;
 }
 
@@ -371,8 +373,10 @@ int dg_describe_launch(int layout, int m, int n, int k, int num_groups, int num_
     return launch(layout, p, m, m, nullptr, units, out);
 }
 
-int dg_gemm_fp8_nt(const void* a, long lda, const float* sa, long ld_sa, const void* b, long ldb, const float* sb,
-                   void* d, long ldd, int m, int n, int k, void* stream) {
+int dg_gemm_fp8_nt_fmt(const void* a, long lda, const float* sa, long ld_sa, const void* b, long ldb, const float* sb,
+                       void* d, long ldd, int m, int n, int k, int a_fmt, int b_fmt, void* stream) {
+    if ((a_fmt != DG_FMT_E4M3 && a_fmt != DG_FMT_E5M2) || (b_fmt != DG_FMT_E4M3 && b_fmt != DG_FMT_E5M2))
+        return DG_ERR_INVALID_ARG;
     int st = check_common(n, k, b, sb, d);
     if (st != DG_OK) return st;
     if (m < 0) return DG_ERR_INVALID_ARG;
@@ -397,7 +401,13 @@ int dg_gemm_fp8_nt(const void* a, long lda, const float* sa, long ld_sa, const v
     p.kblocks = k / kKBlock;
     p.nblocks = (int)ceil_div(n, kKBlock);
     p.num_groups = 1;
+    p.fmt = (a_fmt == DG_FMT_E5M2 ? 1 : 0) | (b_fmt == DG_FMT_E5M2 ? 2 : 0);
     return launch(dg::kDense, p, m, m, static_cast<hipStream_t>(stream), 0, nullptr);
+}
+
+int dg_gemm_fp8_nt(const void* a, long lda, const float* sa, long ld_sa, const void* b, long ldb, const float* sb,
+                   void* d, long ldd, int m, int n, int k, void* stream) {
+    return dg_gemm_fp8_nt_fmt(a, lda, sa, ld_sa, b, ldb, sb, d, ldd, m, n, k, DG_FMT_E4M3, DG_FMT_E4M3, stream);
 }
 
 int dg_m_grouped_gemm_fp8_contiguous(const void* a, const float* sa, long ld_sa, const void* b, const float* sb,

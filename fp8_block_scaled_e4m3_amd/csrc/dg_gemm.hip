@@ -111,12 +111,16 @@ __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC0
 // The 32x32 form needs one scale product per 16 promotion FMAs instead of per 4,
 // and its 32-column sub-tiles never straddle a 128-column scale block when the
 // tile offsets are multiples of 32.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE>
+// FMT: operand formats, bit 0 = A is E5M2, bit 1 = B is E5M2 (else E4M3).  The
+// matrix instruction's format fields take them directly (B rows feed the
+// instruction's first operand, A rows its second).
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT>
 __global__ void __launch_bounds__(WM * WN * 64)
 dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const float* __restrict__ sa_ptr,
                const uint8_t* __restrict__ b_ptr, const float* __restrict__ sb_ptr, uint16_t* __restrict__ d_ptr) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FMT_SRC0 = (FMT >> 1) & 1, FMT_SRC1 = FMT & 1;   // 0 = FP8 E4M3, 1 = BF8 E5M2
     constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int NACC = MF * MF / 64;             // accumulator floats per lane per sub-tile
     constexpr int ROWS = BM + BN;
@@ -672,7 +676,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             const int fn = j / FM, fm = j % FM;
             const int slot = (U * NJ + j) % R;
             if constexpr (MF == 16) {
-                part[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[0], af[fm][0], vacc{}, 0, 0,
+                part[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[0], af[fm][0], vacc{}, FMT_SRC0, FMT_SRC1,
                                                                               0, 0, 0, 0);
                 promote(j - kLag, 0, NACC);
                 issue_loads(j);
@@ -682,7 +686,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 if (fn == FN - 1) af[fm][0] = frag(lna, fm * MF, 0);
                 if (fm == FM - 1) bf[0] = bnext;
             } else {
-                part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[0], af[fm][0], vacc{}, 0, 0,
+                part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[0], af[fm][0], vacc{}, FMT_SRC0, FMT_SRC1,
                                                                              0, 0, 0, 0);
                 promote(j - kLag, 0, NACC / 2);
                 issue_loads(j);
@@ -693,8 +697,8 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 if (j == JB) read_sa(scn, nxt);
                 if (fn == FN - 1) af[fm][0] = frag(lna, fm * MF, 0);
                 __builtin_amdgcn_sched_barrier(0);
-                part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[1], af[fm][1], part[slot], 0,
-                                                                             0, 0, 0, 0, 0);
+                part[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[1], af[fm][1], part[slot], FMT_SRC0,
+                                                                             FMT_SRC1, 0, 0, 0, 0);
                 promote(j - kLag, NACC / 2, NACC);
                 if (fm == FM - 1) bf[1] = fn + 1 < FN ? frag(lc, (fn + 1) * MF, 1) : frag(ln, 0, 1);
                 if (fn == FN - 1) af[fm][1] = frag(lna, fm * MF, 1);
@@ -861,29 +865,40 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     if constexpr (PIPE) wait_vmem_le<0>();
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT>
 static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE>), dim3(grid), dim3(WM * WN * 64), 0, s, p,
-                       p.a, p.sa, p.b, p.sb, p.d);
+    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE, FMT>), dim3(grid), dim3(WM * WN * 64), 0,
+                       s, p, p.a, p.sa, p.b, p.sb, p.d);
     return hipGetLastError();
 }
 
 // The pipelined variant runs the next tile's first NST blocks as the tail of the
 // current one, which needs the K blocks to split into whole groups of NST.  It is
 // compiled only for the configurations whose registers it fits (PIPE_OK).
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK>
+// Configurations with ALL_FMT also have E5M2-operand instances (per-tile variant);
+// the planner gives the others E4M3 operands only.
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool ALL_FMT>
 static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
-    if constexpr (PIPE_OK) {
-        if (p.kblocks % NST == 0) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, true>(p, grid, s);
+    if constexpr (ALL_FMT) {
+        switch (p.fmt) {
+            case 1: return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, 1>(p, grid, s);
+            case 2: return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, 2>(p, grid, s);
+            case 3: return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, 3>(p, grid, s);
+            default: break;
+        }
     }
-    return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false>(p, grid, s);
+    if (p.fmt != 0) return hipErrorInvalidValue;
+    if constexpr (PIPE_OK) {
+        if (p.kblocks % NST == 0) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, true, 0>(p, grid, s);
+    }
+    return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, 0>(p, grid, s);
 }
 
 template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK>
 static hipError_t occupancy_cfg(int* blocks) {
     typedef void (*KernelFn)(const GemmParams, const uint8_t*, const float*, const uint8_t*, const float*, uint16_t*);
-    const KernelFn k0 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, false>;
-    const KernelFn k1 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>;
+    const KernelFn k0 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, false, 0>;
+    const KernelFn k1 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, 0>;
     int b0 = 0, b1 = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, reinterpret_cast<const void*>(k0), WM * WN * 64, 0);
     if (e == hipSuccess)
@@ -892,29 +907,29 @@ static hipError_t occupancy_cfg(int* blocks) {
     return e;
 }
 
-#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF, PIPE_OK)                            \
-    {ID, LAYOUT, BM, BN, WM, WN, EFF, &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>,  \
+#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF, PIPE_OK, ALL_FMT)                              \
+    {ID, LAYOUT, BM, BN, WM, WN, EFF, ALL_FMT, &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, ALL_FMT>, \
      &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>}
 
 static const KernelConfig kConfigs[] = {
     // dense
-    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 2, 1.00, false),
-    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 2, 0.90, false),
-    DG_CFG(2, kDense, 128, 128, 2, 2, 16, 4, 0.55, false),
-    DG_CFG(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false),
-    DG_CFG(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true),
-    DG_CFG(5, kDense, 256, 256, 4, 2, 16, 2, 1.15, true),
+    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 2, 1.00, false, false),
+    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 2, 0.90, false, false),
+    DG_CFG(2, kDense, 128, 128, 2, 2, 16, 4, 0.55, false, false),
+    DG_CFG(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false, true),
+    DG_CFG(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true, false),
+    DG_CFG(5, kDense, 256, 256, 4, 2, 16, 2, 1.15, true, true),
     // contiguous (BLOCK_M = the 128-row segment alignment)
-    DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false),
-    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false),
-    DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95, true),
-    DG_CFG(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false),
+    DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false, false),
+    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false, false),
+    DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95, true, false),
+    DG_CFG(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false, false),
     // masked
-    DG_CFG(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false),
-    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false),
-    DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false),
-    DG_CFG(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90, false),
-    DG_CFG(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false),
+    DG_CFG(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false, false),
+    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false, false),
+    DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false, false),
+    DG_CFG(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90, false, false),
+    DG_CFG(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, false),
 };
 
 const KernelConfig* kernel_configs(int* count) {

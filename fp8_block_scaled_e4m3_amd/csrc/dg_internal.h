@@ -25,6 +25,7 @@ struct GemmParams {
     int num_tiles;         // dense/contiguous: exact; masked: upper bound
     int group_m;           // raster: tiles_m rows visited together
     int xcd_remap;         // 1 when the grid is a multiple of the XCD count
+    int fmt;               // operand formats: bit 0 set = A is E5M2, bit 1 set = B is E5M2 (else E4M3)
 };
 
 struct KernelConfig {
@@ -32,6 +33,7 @@ struct KernelConfig {
     int layout;
     int bm, bn, wm, wn;
     double eff;            // relative throughput used by the planner
+    bool all_formats;      // compiled for E5M2 operands too (else E4M3 only)
     hipError_t (*launch)(const GemmParams&, int grid, hipStream_t);
     hipError_t (*occupancy)(int* blocks_per_cu);
 };

@@ -50,6 +50,12 @@ enum {
     DG_ERR_HIP = -4            /* a HIP runtime call or the kernel launch failed */
 };
 
+/* FP8 operand formats (dg_gemm_fp8_nt_fmt). */
+enum {
+    DG_FMT_E4M3 = 0,           /* OCP E4M3FN: max 448, no infinities */
+    DG_FMT_E5M2 = 1            /* OCP E5M2: max 57344, infinities */
+};
+
 /* Human-readable name of a status code.  Never NULL; the string is static. */
 const char* dg_status_string(int status);
 
@@ -79,6 +85,17 @@ int dg_gemm_fp8_nt(const void* a, long lda,
                    const float* sb,
                    void* d, long ldd,
                    int m, int n, int k, void* stream);
+
+/* The dense NT GEMM with each operand's FP8 format chosen: DG_FMT_E4M3 or
+ * DG_FMT_E5M2 for a and for b independently (the hnwysp.cn DeepGEMM blog,
+ * section 2.3, lists E4M3 and E5M2 as the FP8 operand formats).  Scales, layouts,
+ * promotion and output are exactly those of dg_gemm_fp8_nt, which is this call
+ * with two E4M3 operands.  An unknown format is DG_ERR_INVALID_ARG.  E5M2
+ * operands run on a subset of the tile configurations. */
+int dg_gemm_fp8_nt_fmt(const void* a, long lda, const float* sa, long ld_sa,
+                       const void* b, long ldb, const float* sb,
+                       void* d, long ldd, int m, int n, int k,
+                       int a_fmt, int b_fmt, void* stream);
 
 /* M-grouped GEMM, contiguous layout (the README's contiguous-layout paragraph:
  * experts share N and K; their token segments are concatenated along M and each
@@ -142,8 +159,9 @@ int dg_quantize_fp8_128x128(const void* x, int x_dtype, long ldx, int rows, int 
 int dg_set_kernel_config(int config_id);
 
 /* Enumerate the compiled kernel configurations: for index 0, 1, ... fills
- * out[0..4] = config id, layout, block_m, block_n, waves per workgroup and returns
- * DG_OK; past the last one returns DG_ERR_INVALID_ARG.  Host only. */
+ * out[0..5] = config id, layout, block_m, block_n, waves per workgroup, and 1 if
+ * the configuration also runs E5M2 operands (dg_gemm_fp8_nt_fmt) else 0, and
+ * returns DG_OK; past the last one returns DG_ERR_INVALID_ARG.  Host only. */
 int dg_kernel_config_info(int index, int* out);
 
 /* Host-only tile planner, exposed for inspection and tests; it touches no device.

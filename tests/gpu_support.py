@@ -42,6 +42,10 @@ def sentinel_like(shape):
 
 
 def bits(t) -> np.ndarray:
+    """BF16 output (as bfloat16 or its int16 bit pattern) -> uint16 bits on the host."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
     return t.cpu().numpy().view(np.uint16)
 
 

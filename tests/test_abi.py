@@ -68,6 +68,25 @@ def _call_dense(lib, a=16, sa=16, b=16, sb=16, d=16, lda=512, ld_sa=128, ldb=512
     return lib.dg_gemm_fp8_nt(P(a), lda, P(sa), ld_sa, P(b), ldb, P(sb), P(d), ldd, m, n, k, None)
 
 
+def _call_dense_fmt(lib, a_fmt, b_fmt, k=512):
+    P = ctypes.c_void_p
+    return lib.dg_gemm_fp8_nt_fmt(P(16), 512, P(16), 128, P(16), 512, P(16), P(16), 128, 128, 128, k,
+                                  a_fmt, b_fmt, None)
+
+
+def test_format_entry_validation(lib):
+    """Unknown format codes are rejected before anything else; the E5M2 variants are
+    compiled for dense configurations only."""
+    assert (dg.DG_FMT_E4M3, dg.DG_FMT_E5M2) == (0, 1)
+    for fa, fb in ((2, 0), (0, -1), (7, 7)):
+        assert _call_dense_fmt(lib, fa, fb) == dg.DG_ERR_INVALID_ARG
+    for fa, fb in ((0, 1), (1, 0), (1, 1)):
+        assert _call_dense_fmt(lib, fa, fb, k=500) == dg.DG_ERR_UNSUPPORTED
+    cfgs = dg.dg_kernel_config_info()
+    assert any(c["all_formats"] for c in cfgs if c["layout"] == 0)
+    assert not any(c["all_formats"] for c in cfgs if c["layout"] != 0)
+
+
 def test_dense_validation_before_any_device_work(lib):
     assert _call_dense(lib, k=500) == dg.DG_ERR_UNSUPPORTED
     assert _call_dense(lib, k=0) == dg.DG_ERR_UNSUPPORTED

@@ -1,0 +1,142 @@
+"""GPU parity for the dense GEMM with E5M2 operands (either side, or both).
+
+The blog's FP8 section lets each operand be E4M3 or E5M2.  Every combination is
+compared with the oracle element by element on small and ragged shapes in each
+tile configuration that carries the E5M2 variants, through the planner, and on a
+larger shape on sampled rows; the E4M3/E4M3 case of the same entry point must be
+bit-identical to the plain dense entry point.
+"""
+import numpy as np
+import pytest
+
+import fp8_block_scaled_e4m3_amd as dg
+import workloads as W
+from tests.gpu_support import bits, check_values, require_gpu, sample_rows, say, sentinel_like, upload
+
+pytestmark = pytest.mark.gpu
+
+COMBOS = [("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2")]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    dev = require_gpu()
+    dg.load_library()
+    yield dev
+    dg.dg_set_kernel_config(-1)
+    dg.dg_set_num_cus(0)
+
+
+def fmt_configs():
+    return [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and c["all_formats"]]
+
+
+def run_fmt(dd, cfg=-1, pad_cols=16):
+    import torch
+    dv = upload(dd)
+    m, n = dd["a"].shape[0], dd["b"].shape[0]
+    full = sentinel_like((m, n + pad_cols))
+    dg.dg_set_kernel_config(cfg)
+    try:
+        dg.dg_gemm_fp8_nt_fmt(dv["a"], dv["sa"], dv["b"], dv["sb"], full[:, :n],
+                              a_fmt=dd["a_fmt"], b_fmt=dd["b_fmt"])
+        torch.cuda.synchronize()
+    finally:
+        dg.dg_set_kernel_config(-1)
+    fb = bits(full)
+    return fb[:, :n], fb
+
+
+def oracle_fmt(orc, dd, rows=None):
+    a, sa = dd["a"], dd["sa"]
+    if rows is not None:
+        a, sa = a[rows], sa[:, rows]
+    return orc.gemm_fp8_nt(a, sa, dd["b"], dd["sb"], a_fmt=dd["a_fmt"], b_fmt=dd["b_fmt"])
+
+
+def test_format_configs_exist():
+    assert len(fmt_configs()) >= 2
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", COMBOS)
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (128, 128, 512), (300, 208, 384), (513, 1040, 1024)])
+def test_e5m2_ragged_shapes(orc, a_fmt, b_fmt, m, n, k):
+    dd = W.make_dense(m, n, k, seed=7 * m + n + k, a_fmt=a_fmt, b_fmt=b_fmt)
+    ref = oracle_fmt(orc, dd)
+    outs = []
+    for cfg in [-1] + fmt_configs():
+        say(f"dense {a_fmt}x{b_fmt} {m}x{n}x{k} cfg={cfg}")
+        out, full = run_fmt(dd, cfg)
+        check_values(out, ref, f"{a_fmt}x{b_fmt} {m}x{n}x{k} cfg{cfg}")
+        assert np.all(full[:, n:] == W.SENTINEL_BF16), "wrote past column n"
+        outs.append(out)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", COMBOS)
+def test_e5m2_chained_tiles(orc, a_fmt, b_fmt):
+    """Few workgroups, many tiles each, K/128 a multiple of the stage count so the
+    prefetch of the next tile runs across tile boundaries."""
+    dd = W.make_dense(300, 464, 512, seed=91, a_fmt=a_fmt, b_fmt=b_fmt)
+    ref = oracle_fmt(orc, dd)
+    dg.dg_set_num_cus(3)
+    try:
+        for cfg in fmt_configs():
+            say(f"dense {a_fmt}x{b_fmt} 300x464x512 cfg={cfg} cu cap 3")
+            out, _ = run_fmt(dd, cfg)
+            check_values(out, ref, f"{a_fmt}x{b_fmt} chained cfg{cfg}")
+    finally:
+        dg.dg_set_num_cus(0)
+
+
+def test_e5m2_large_sampled(orc):
+    dd = W.make_dense(2048, 4096, 2048, seed=5, a_fmt="e5m2", b_fmt="e4m3")
+    say("dense e5m2xe4m3 2048x4096x2048 planned")
+    out, full = run_fmt(dd)
+    assert np.all(full[:, 4096:] == W.SENTINEL_BF16)
+    rows = sample_rows(2048, 256, 32)
+    check_values(out[rows], oracle_fmt(orc, dd, rows), "e5m2xe4m3 2048x4096x2048 sampled rows")
+
+
+def test_e4m3_pair_matches_plain_entry():
+    import torch
+    dd = W.make_dense(200, 336, 640, seed=3)
+    dv = upload(dd)
+    d0 = torch.zeros((200, 336), dtype=torch.bfloat16, device="cuda:0")
+    d1 = torch.ones((200, 336), dtype=torch.bfloat16, device="cuda:0")
+    dg.dg_gemm_fp8_nt(dv["a"], dv["sa"], dv["b"], dv["sb"], d0)
+    dg.dg_gemm_fp8_nt_fmt(dv["a"], dv["sa"], dv["b"], dv["sb"], d1, a_fmt="e4m3", b_fmt="e4m3")
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d0), bits(d1))
+
+
+def test_float8_dtypes_carry_the_format(orc):
+    import torch
+    dd = W.make_dense(64, 128, 256, seed=11, a_fmt="e5m2", b_fmt="e5m2")
+    dv = upload(dd)
+    a8, b8 = dv["a"].view(torch.float8_e5m2), dv["b"].view(torch.float8_e5m2)
+    d = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda:0")
+    dg.dg_gemm_fp8_nt_fmt(a8, dv["sa"], b8, dv["sb"], d)
+    torch.cuda.synchronize()
+    check_values(bits(d), oracle_fmt(orc, dd), "float8_e5m2 tensors")
+    with pytest.raises(ValueError):
+        dg.dg_gemm_fp8_nt_fmt(a8, dv["sa"], b8, dv["sb"], d, a_fmt="e4m3")
+
+
+def test_forced_config_without_formats_is_unsupported():
+    import torch
+    plain = [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and not c["all_formats"]]
+    assert plain
+    dd = W.make_dense(64, 128, 256, seed=12, a_fmt="e5m2", b_fmt="e4m3")
+    dv = upload(dd)
+    d = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda:0")
+    dg.dg_set_kernel_config(plain[0])
+    try:
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_gemm_fp8_nt_fmt(dv["a"], dv["sa"], dv["b"], dv["sb"], d, a_fmt="e5m2", b_fmt="e4m3")
+    finally:
+        dg.dg_set_kernel_config(-1)
+    assert e.value.status == dg.DG_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(d).item() == 0

@@ -1,10 +1,11 @@
 """Seeded synthetic inputs for the fine-grained-scaled FP8 E4M3 NT GEMM.
 
 This module is shared by the tests, the smoke check and the bench.  It draws
-random fp32 data and casts it to E4M3 with per-block fp32 scales; it holds none
-of the GEMM's arithmetic (no decode, no dot products, no promotion, no BF16
-rounding).  The fp8 cast itself is torch's float32 -> float8_e4m3fn conversion
-(round to nearest even); the scale arithmetic is numpy fp32.  The oracle has its
+random fp32 data and casts it to E4M3 (or E5M2, for the dense GEMM's format
+option) with per-block fp32 scales; it holds none of the GEMM's arithmetic (no
+decode, no dot products, no promotion, no BF16 rounding).  The fp8 cast itself
+is torch's float32 -> float8_e4m3fn / float8_e5m2 conversion (round to nearest
+even); the scale arithmetic is numpy fp32 (amax / 448, or amax / 57344 for E5M2).  The oracle has its
 own, independently written quantiser, and a test checks that both agree bit
 for bit.
 
@@ -35,6 +36,8 @@ import numpy as np
 KBLOCK = 128
 M_ALIGN = 128          # contiguous-layout segment alignment (= the kernels' M block)
 E4M3_MAX = 448.0       # largest finite OCP E4M3FN value
+E5M2_MAX = 57344.0     # largest finite OCP E5M2 value
+FP8_MAX = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX}
 
 
 @dataclass(frozen=True)
@@ -109,55 +112,57 @@ def make_fp32_operand(rows: int, k: int, block_rows: int, seed: int = 0) -> np.n
     return _scaled_normals(np.random.default_rng(seed), rows, k, block_rows)
 
 
-def _cast_e4m3(y: np.ndarray) -> np.ndarray:
+def _cast_fp8(y: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
     import torch
     t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32))
-    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+    return t.to(dt).view(torch.uint8).numpy().copy()
 
 
-def _block_scales(amax: np.ndarray) -> np.ndarray:
+def _block_scales(amax: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
     amax = amax.astype(np.float32)
-    s = amax / np.float32(E4M3_MAX)
+    s = amax / np.float32(FP8_MAX[fmt])
     return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
 
 
-def quant_rows_1x128(x: np.ndarray):
-    """fp32 [rows, k] -> (E4M3 bytes [rows, k], sa fp32 [Kb, ld_sa])."""
+def quant_rows_1x128(x: np.ndarray, fmt: str = "e4m3"):
+    """fp32 [rows, k] -> (FP8 bytes [rows, k], sa fp32 [Kb, ld_sa]); fmt "e4m3" or "e5m2"."""
     rows, k = x.shape
     kb = ceil_div(k, KBLOCK)
     kp = kb * KBLOCK
     xp = np.zeros((rows, kp), np.float32)
     xp[:, :k] = x
     xb = xp.reshape(rows, kb, KBLOCK)
-    s = _block_scales(np.abs(xb).max(axis=2))                      # [rows, kb]
-    y = np.clip(xb / s[:, :, None], -E4M3_MAX, E4M3_MAX).reshape(rows, kp)[:, :k]
-    q = _cast_e4m3(y)
+    s = _block_scales(np.abs(xb).max(axis=2), fmt)                 # [rows, kb]
+    y = np.clip(xb / s[:, :, None], -FP8_MAX[fmt], FP8_MAX[fmt]).reshape(rows, kp)[:, :k]
+    q = _cast_fp8(y, fmt)
     sa = np.zeros((kb, ld_sa_for(rows)), np.float32)
     sa[:, :rows] = s.T
     return q, sa
 
 
-def quant_blocks_128x128(x: np.ndarray):
-    """fp32 [n, k] -> (E4M3 bytes [n, k], sb fp32 [ceil(n/128), Kb])."""
+def quant_blocks_128x128(x: np.ndarray, fmt: str = "e4m3"):
+    """fp32 [n, k] -> (FP8 bytes [n, k], sb fp32 [ceil(n/128), Kb]); fmt "e4m3" or "e5m2"."""
     n, k = x.shape
     nb, kb = ceil_div(n, KBLOCK), ceil_div(k, KBLOCK)
     xp = np.zeros((nb * KBLOCK, kb * KBLOCK), np.float32)
     xp[:n, :k] = x
     xb = xp.reshape(nb, KBLOCK, kb, KBLOCK)
-    s = _block_scales(np.abs(xb).max(axis=(1, 3)))                  # [nb, kb]
-    y = np.clip(xb / s[:, None, :, None], -E4M3_MAX, E4M3_MAX)
+    s = _block_scales(np.abs(xb).max(axis=(1, 3)), fmt)             # [nb, kb]
+    y = np.clip(xb / s[:, None, :, None], -FP8_MAX[fmt], FP8_MAX[fmt])
     y = y.reshape(nb * KBLOCK, kb * KBLOCK)[:n, :k]
-    return _cast_e4m3(y), s
+    return _cast_fp8(y, fmt), s
 
 
-def make_dense(m: int, n: int, k: int, seed: int = 0) -> dict:
+def make_dense(m: int, n: int, k: int, seed: int = 0, a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> dict:
     rng = np.random.default_rng(seed)
     xa = _scaled_normals(rng, m, k, 1)
-    a, sa = quant_rows_1x128(xa)
+    a, sa = quant_rows_1x128(xa, a_fmt)
     del xa
     xb = _scaled_normals(rng, n, k, KBLOCK)
-    b, sb = quant_blocks_128x128(xb)
-    return {"kind": "dense", "a": a, "sa": sa, "b": b, "sb": sb, "m": m, "n": n, "k": k}
+    b, sb = quant_blocks_128x128(xb, b_fmt)
+    return {"kind": "dense", "a": a, "sa": sa, "b": b, "sb": sb, "m": m, "n": n, "k": k,
+            "a_fmt": a_fmt, "b_fmt": b_fmt}
 
 
 def make_contiguous(counts, n: int, k: int, seed: int = 0, align: int = M_ALIGN) -> dict:
