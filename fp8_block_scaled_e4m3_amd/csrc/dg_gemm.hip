@@ -490,9 +490,11 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // stage kb % NST as soon as block kb's barrier has freed it: copy t at step
     // JB + 1 + t*CPN/CPD of block kb (two steps apart when a block is long enough),
     // running on into the first steps of block kb+1, never past its barrier
-    // (where, for NST=2, they must have landed).
+    // (where, for NST=2, they must have landed).  The masked layout streams B
+    // with little MFMA work per byte, so there the copies go out one step apart:
+    // the last one leaves earlier and has longer to land before the barrier.
     constexpr int NDMA = NSLOT + 1;
-    constexpr int CPN = 2 * NDMA + 4 <= NJ ? 2 : (NDMA + 4 <= NJ ? 1 : NJ);
+    constexpr int CPN = LAYOUT == kMasked ? 1 : (2 * NDMA + 4 <= NJ ? 2 : (NDMA + 4 <= NJ ? 1 : NJ));
     constexpr int CPD = CPN == NJ ? NDMA : 1;
     static_assert((NDMA - 1) * CPN / CPD + 1 <= NJ, "copies must be issued before the next barrier");
     constexpr int NFIRST = [] {   // copies issued in the freeing block
