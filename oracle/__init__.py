@@ -86,6 +86,10 @@ def _load():
     lib.orc_m_grouped_contiguous.restype = I
     lib.orc_m_grouped_masked.argtypes = [P, P, L, P, P, P, P, P, I, I, I, I, I]
     lib.orc_m_grouped_masked.restype = I
+    lib.orc_m_grouped_contiguous_fmt.argtypes = [P, P, L, P, P, P, P, P, I, I, I, I, I, I, I]
+    lib.orc_m_grouped_contiguous_fmt.restype = I
+    lib.orc_m_grouped_masked_fmt.argtypes = [P, P, L, P, P, P, P, P, I, I, I, I, I, I, I]
+    lib.orc_m_grouped_masked_fmt.restype = I
     _lib = lib
     return lib
 
@@ -188,10 +192,11 @@ def gemm_fp8_nt(a, sa, b, sb, *, d_init=None, want_acc=False, nthreads=0, a_fmt=
     return (d, acc) if want_acc else d
 
 
-def m_grouped_contiguous(a, sa, b, sb, m_indices, *, d_init=None, want_acc=False, nthreads=0):
-    """a: E4M3 [m_total, k]; sa: fp32 [Kb, ld_sa>=m_total]; b: E4M3 [G, n, k];
-    sb: fp32 [G, ceil(n/128), Kb]; m_indices: int32 [m_total] (group or -1).
-    Rows with -1 keep ``d_init`` (zeros by default)."""
+def m_grouped_contiguous(a, sa, b, sb, m_indices, *, d_init=None, want_acc=False, nthreads=0,
+                         a_fmt="e4m3", b_fmt="e4m3"):
+    """a: FP8 [m_total, k]; sa: fp32 [Kb, ld_sa>=m_total]; b: FP8 [G, n, k];
+    sb: fp32 [G, ceil(n/128), Kb]; m_indices: int32 [m_total] (group or -1); each
+    operand E4M3 or E5M2.  Rows with -1 keep ``d_init`` (zeros by default)."""
     a, b, sa, sb = _u8(a), _u8(b), _f32(sa), _f32(sb)
     mi = np.ascontiguousarray(np.asarray(m_indices, dtype=np.int32))
     m_total, k = a.shape
@@ -200,15 +205,21 @@ def m_grouped_contiguous(a, sa, b, sb, m_indices, *, d_init=None, want_acc=False
     assert mi.max(initial=-1) < g
     d = np.zeros((m_total, n), np.uint16) if d_init is None else np.array(d_init, np.uint16, copy=True)
     acc = np.full((m_total, n), np.nan) if want_acc else None
-    _load().orc_m_grouped_contiguous(_ptr(a), _ptr(sa), sa.shape[1], _ptr(b), _ptr(sb),
-                                     _ptr(d), _ptr(acc), _ptr(mi), m_total, n, k, g, int(nthreads))
+    if a_fmt == "e4m3" and b_fmt == "e4m3":
+        _load().orc_m_grouped_contiguous(_ptr(a), _ptr(sa), sa.shape[1], _ptr(b), _ptr(sb),
+                                         _ptr(d), _ptr(acc), _ptr(mi), m_total, n, k, g, int(nthreads))
+    else:
+        _load().orc_m_grouped_contiguous_fmt(_ptr(a), _ptr(sa), sa.shape[1], _ptr(b), _ptr(sb),
+                                             _ptr(d), _ptr(acc), _ptr(mi), m_total, n, k, g,
+                                             FORMATS[a_fmt], FORMATS[b_fmt], int(nthreads))
     return (d, acc) if want_acc else d
 
 
-def m_grouped_masked(a, sa, b, sb, masked_m, *, d_init=None, want_acc=False, nthreads=0):
-    """a: E4M3 [G, max_m, k]; sa: fp32 [G, Kb, ld_sa>=max_m]; b: E4M3 [G, n, k];
-    sb: fp32 [G, ceil(n/128), Kb]; masked_m: int32 [G].  Rows >= masked_m[g]
-    keep ``d_init`` (zeros by default)."""
+def m_grouped_masked(a, sa, b, sb, masked_m, *, d_init=None, want_acc=False, nthreads=0,
+                     a_fmt="e4m3", b_fmt="e4m3"):
+    """a: FP8 [G, max_m, k]; sa: fp32 [G, Kb, ld_sa>=max_m]; b: FP8 [G, n, k];
+    sb: fp32 [G, ceil(n/128), Kb]; masked_m: int32 [G]; each operand E4M3 or
+    E5M2.  Rows >= masked_m[g] keep ``d_init`` (zeros by default)."""
     a, b, sa, sb = _u8(a), _u8(b), _f32(sa), _f32(sb)
     mm = np.ascontiguousarray(np.asarray(masked_m, dtype=np.int32))
     g, max_m, k = a.shape
@@ -217,6 +228,11 @@ def m_grouped_masked(a, sa, b, sb, masked_m, *, d_init=None, want_acc=False, nth
     assert sa.shape[:2] == (g, -(-k // KBLOCK)) and sa.shape[2] >= max_m
     d = np.zeros((g, max_m, n), np.uint16) if d_init is None else np.array(d_init, np.uint16, copy=True)
     acc = np.full((g, max_m, n), np.nan) if want_acc else None
-    _load().orc_m_grouped_masked(_ptr(a), _ptr(sa), sa.shape[2], _ptr(b), _ptr(sb),
-                                 _ptr(d), _ptr(acc), _ptr(mm), g, max_m, n, k, int(nthreads))
+    if a_fmt == "e4m3" and b_fmt == "e4m3":
+        _load().orc_m_grouped_masked(_ptr(a), _ptr(sa), sa.shape[2], _ptr(b), _ptr(sb),
+                                     _ptr(d), _ptr(acc), _ptr(mm), g, max_m, n, k, int(nthreads))
+    else:
+        _load().orc_m_grouped_masked_fmt(_ptr(a), _ptr(sa), sa.shape[2], _ptr(b), _ptr(sb),
+                                         _ptr(d), _ptr(acc), _ptr(mm), g, max_m, n, k,
+                                         FORMATS[a_fmt], FORMATS[b_fmt], int(nthreads))
     return (d, acc) if want_acc else d

@@ -423,11 +423,12 @@ int orc_gemm_fp8_nt_fmt(const uint8_t* a, long lda, const float* sa, long ld_sa,
 
 /* M-grouped contiguous: A [m_total][k], sa [Kb][ld_sa], B [G][n][k],
  * sb [G][ceil(n/128)][Kb], D [m_total][n]; m_indices[row] = group or -1.
- * Rows with -1 are not written. */
-int orc_m_grouped_contiguous(const uint8_t* a, const float* sa, long ld_sa,
-                             const uint8_t* b, const float* sb,
-                             uint16_t* d, double* acc_out, const int* m_indices,
-                             int m_total, int n, int k, int num_groups, int nthreads)
+ * Rows with -1 are not written.  Operand formats as in orc_gemm_fp8_nt_fmt. */
+int orc_m_grouped_contiguous_fmt(const uint8_t* a, const float* sa, long ld_sa,
+                                 const uint8_t* b, const float* sb,
+                                 uint16_t* d, double* acc_out, const int* m_indices,
+                                 int m_total, int n, int k, int num_groups,
+                                 int a_fmt, int b_fmt, int nthreads)
 {
     orc_job J;
     int kbn = (k + ORC_KBLOCK - 1) / ORC_KBLOCK, nbn = (n + ORC_KBLOCK - 1) / ORC_KBLOCK;
@@ -438,16 +439,27 @@ int orc_m_grouped_contiguous(const uint8_t* a, const float* sa, long ld_sa,
     J.sb = sb; J.sb_group_stride = (long)nbn * kbn;
     J.d = d; J.ldd = n; J.acc_out = acc_out;
     J.m = m_total; J.n = n; J.k = k; J.layout = 1; J.m_indices = m_indices;
+    J.a_fmt = a_fmt != 0; J.b_fmt = b_fmt != 0;
     return run_rows(J, nthreads);
+}
+
+int orc_m_grouped_contiguous(const uint8_t* a, const float* sa, long ld_sa,
+                             const uint8_t* b, const float* sb,
+                             uint16_t* d, double* acc_out, const int* m_indices,
+                             int m_total, int n, int k, int num_groups, int nthreads)
+{
+    return orc_m_grouped_contiguous_fmt(a, sa, ld_sa, b, sb, d, acc_out, m_indices, m_total, n, k, num_groups,
+                                        0, 0, nthreads);
 }
 
 /* M-grouped masked: A [G][max_m][k], sa [G][Kb][ld_sa], B [G][n][k],
  * sb [G][ceil(n/128)][Kb], D [G][max_m][n]; rows >= masked_m[g] (clamped to
- * [0, max_m]) are not written. */
-int orc_m_grouped_masked(const uint8_t* a, const float* sa, long ld_sa,
-                         const uint8_t* b, const float* sb,
-                         uint16_t* d, double* acc_out, const int* masked_m,
-                         int num_groups, int max_m, int n, int k, int nthreads)
+ * [0, max_m]) are not written.  Operand formats as in orc_gemm_fp8_nt_fmt. */
+int orc_m_grouped_masked_fmt(const uint8_t* a, const float* sa, long ld_sa,
+                             const uint8_t* b, const float* sb,
+                             uint16_t* d, double* acc_out, const int* masked_m,
+                             int num_groups, int max_m, int n, int k,
+                             int a_fmt, int b_fmt, int nthreads)
 {
     orc_job J;
     int kbn = (k + ORC_KBLOCK - 1) / ORC_KBLOCK, nbn = (n + ORC_KBLOCK - 1) / ORC_KBLOCK;
@@ -458,5 +470,15 @@ int orc_m_grouped_masked(const uint8_t* a, const float* sa, long ld_sa,
     J.d = d; J.ldd = n; J.acc_out = acc_out;
     J.m = num_groups * max_m; J.n = n; J.k = k; J.layout = 2;
     J.masked_m = masked_m; J.max_m = max_m;
+    J.a_fmt = a_fmt != 0; J.b_fmt = b_fmt != 0;
     return run_rows(J, nthreads);
+}
+
+int orc_m_grouped_masked(const uint8_t* a, const float* sa, long ld_sa,
+                         const uint8_t* b, const float* sb,
+                         uint16_t* d, double* acc_out, const int* masked_m,
+                         int num_groups, int max_m, int n, int k, int nthreads)
+{
+    return orc_m_grouped_masked_fmt(a, sa, ld_sa, b, sb, d, acc_out, masked_m, num_groups, max_m, n, k,
+                                    0, 0, nthreads);
 }

@@ -419,6 +419,55 @@ def test_masked_equals_dense_and_keeps_sentinel(orc):
         assert np.all(out[g, c:] == W.SENTINEL_BF16)
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2")])
+def test_grouped_fmt_equal_dense_fmt_per_group(orc, fa, fb):
+    """With E5M2 operands the grouped layouts still equal the dense GEMM (pinned against
+    exact rationals for every format pair) group by group, padding and masked rows
+    untouched."""
+    counts = [130, 0, 3]
+    cd = W.make_contiguous(counts, n=144, k=256, seed=21, a_fmt=fa, b_fmt=fb)
+    sentinel = np.full((cd["m_total"], 144), W.SENTINEL_BF16, np.uint16)
+    out = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], cd["m_indices"], d_init=sentinel,
+                                   a_fmt=fa, b_fmt=fb)
+    off = 0
+    for g, (c, p) in enumerate(zip(counts, W.padded(counts))):
+        if c:
+            ref = orc.gemm_fp8_nt(cd["a"][off:off + c], cd["sa"][:, off:off + c], cd["b"][g], cd["sb"][g],
+                                  a_fmt=fa, b_fmt=fb)
+            assert np.array_equal(out[off:off + c], ref)
+        assert np.all(out[off + c:off + p] == W.SENTINEL_BF16)
+        off += p
+    mm = [0, 5, 40]
+    md = W.make_masked(3, 40, 144, 256, seed=22, masked_m=mm, a_fmt=fa, b_fmt=fb)
+    sentinel = np.full((3, 40, 144), W.SENTINEL_BF16, np.uint16)
+    out = orc.m_grouped_masked(md["a"], md["sa"], md["b"], md["sb"], md["masked_m"], d_init=sentinel,
+                               a_fmt=fa, b_fmt=fb)
+    for g, c in enumerate(mm):
+        if c:
+            ref = orc.gemm_fp8_nt(md["a"][g, :c], md["sa"][g][:, :c], md["b"][g], md["sb"][g], a_fmt=fa, b_fmt=fb)
+            assert np.array_equal(out[g, :c], ref)
+        assert np.all(out[g, c:] == W.SENTINEL_BF16)
+
+
+def test_grouped_fmt_e4m3_matches_plain_path(orc):
+    counts = [70, 2]
+    cd = W.make_contiguous(counts, n=48, k=256, seed=23)
+    plain = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], cd["m_indices"])
+    lib = orc._load()
+    d = np.zeros_like(plain)
+    lib.orc_m_grouped_contiguous_fmt(orc._ptr(cd["a"]), orc._ptr(cd["sa"]), cd["sa"].shape[1], orc._ptr(cd["b"]),
+                                     orc._ptr(cd["sb"]), orc._ptr(d), None, orc._ptr(cd["m_indices"]),
+                                     cd["m_total"], 48, 256, 2, 0, 0, 1)
+    assert np.array_equal(d, plain)
+    md = W.make_masked(2, 24, 48, 256, seed=24, masked_m=[24, 3])
+    plain = orc.m_grouped_masked(md["a"], md["sa"], md["b"], md["sb"], md["masked_m"])
+    d = np.zeros_like(plain)
+    lib.orc_m_grouped_masked_fmt(orc._ptr(md["a"]), orc._ptr(md["sa"]), md["sa"].shape[2], orc._ptr(md["b"]),
+                                 orc._ptr(md["sb"]), orc._ptr(d), None, orc._ptr(md["masked_m"]),
+                                 2, 24, 48, 256, 0, 0, 1)
+    assert np.array_equal(d, plain)
+
+
 def test_masked_clamps_out_of_range_counts(orc):
     dd = W.make_masked(2, 16, 32, 128, seed=14, masked_m=[-5, 99])
     sentinel = np.full((2, 16, 32), W.SENTINEL_BF16, np.uint16)

@@ -165,7 +165,8 @@ def make_dense(m: int, n: int, k: int, seed: int = 0, a_fmt: str = "e4m3", b_fmt
             "a_fmt": a_fmt, "b_fmt": b_fmt}
 
 
-def make_contiguous(counts, n: int, k: int, seed: int = 0, align: int = M_ALIGN) -> dict:
+def make_contiguous(counts, n: int, k: int, seed: int = 0, align: int = M_ALIGN,
+                    a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> dict:
     counts = [int(c) for c in counts]
     pads = padded(counts, align)
     m_total = sum(pads)
@@ -176,27 +177,29 @@ def make_contiguous(counts, n: int, k: int, seed: int = 0, align: int = M_ALIGN)
         off += p
     rng = np.random.default_rng(seed)
     xa = _scaled_normals(rng, m_total, k, 1)
-    a, sa = quant_rows_1x128(xa)
+    a, sa = quant_rows_1x128(xa, a_fmt)
     del xa
     G = len(counts)
     b = np.empty((G, n, k), np.uint8)
     sb = np.empty((G, ceil_div(n, KBLOCK), ceil_div(k, KBLOCK)), np.float32)
     for g in range(G):
         xb = _scaled_normals(rng, n, k, KBLOCK)
-        b[g], sb[g] = quant_blocks_128x128(xb)
+        b[g], sb[g] = quant_blocks_128x128(xb, b_fmt)
         del xb
     return {"kind": "contiguous", "a": a, "sa": sa, "b": b, "sb": sb, "m_indices": m_indices,
-            "counts": counts, "m_total": m_total, "n": n, "k": k, "groups": G}
+            "counts": counts, "m_total": m_total, "n": n, "k": k, "groups": G,
+            "a_fmt": a_fmt, "b_fmt": b_fmt}
 
 
-def make_masked(groups: int, max_m: int, n: int, k: int, seed: int = 0, masked_m=None) -> dict:
+def make_masked(groups: int, max_m: int, n: int, k: int, seed: int = 0, masked_m=None,
+                a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> dict:
     rng = np.random.default_rng(seed)
     xa = _scaled_normals(rng, groups * max_m, k, 1)
     kb = ceil_div(k, KBLOCK)
     a = np.empty((groups, max_m, k), np.uint8)
     sa = np.zeros((groups, kb, ld_sa_for(max_m)), np.float32)
     for g in range(groups):
-        q, s = quant_rows_1x128(xa[g * max_m:(g + 1) * max_m])
+        q, s = quant_rows_1x128(xa[g * max_m:(g + 1) * max_m], a_fmt)
         a[g] = q
         sa[g] = s
     del xa
@@ -204,13 +207,13 @@ def make_masked(groups: int, max_m: int, n: int, k: int, seed: int = 0, masked_m
     sb = np.empty((groups, ceil_div(n, KBLOCK), kb), np.float32)
     for g in range(groups):
         xb = _scaled_normals(rng, n, k, KBLOCK)
-        b[g], sb[g] = quant_blocks_128x128(xb)
+        b[g], sb[g] = quant_blocks_128x128(xb, b_fmt)
         del xb
     mm = rng.integers(0, max_m + 1, size=groups).astype(np.int32)
     if masked_m is not None:
         mm = np.asarray(masked_m, dtype=np.int32)
     return {"kind": "masked", "a": a, "sa": sa, "b": b, "sb": sb, "masked_m": mm,
-            "groups": groups, "max_m": max_m, "n": n, "k": k}
+            "groups": groups, "max_m": max_m, "n": n, "k": k, "a_fmt": a_fmt, "b_fmt": b_fmt}
 
 
 def make(w: Workload | str) -> dict:
