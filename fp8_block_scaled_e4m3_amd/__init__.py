@@ -64,6 +64,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_m_grouped_gemm_fp8_contiguous.restype = I
     lib.dg_m_grouped_gemm_fp8_masked.argtypes = [P, P, L, P, P, P, P, I, I, I, I, P]
     lib.dg_m_grouped_gemm_fp8_masked.restype = I
+    lib.dg_m_grouped_gemm_fp8_contiguous_fmt.argtypes = [P, P, L, P, P, P, P, I, I, I, I, I, I, P]
+    lib.dg_m_grouped_gemm_fp8_contiguous_fmt.restype = I
+    lib.dg_m_grouped_gemm_fp8_masked_fmt.argtypes = [P, P, L, P, P, P, P, I, I, I, I, I, I, P]
+    lib.dg_m_grouped_gemm_fp8_masked_fmt.restype = I
     lib.dg_quantize_fp8_1x128.argtypes = [P, I, L, I, I, P, L, P, L, P]
     lib.dg_quantize_fp8_1x128.restype = I
     lib.dg_quantize_fp8_128x128.argtypes = [P, I, L, I, I, P, L, P, P]
@@ -196,16 +200,23 @@ def dg_gemm_fp8_nt_fmt(a, sa, b, sb, d, a_fmt=None, b_fmt=None, stream=None) -> 
 
 
 def dg_m_grouped_gemm_fp8_contiguous(a, sa, b, sb, d, m_indices, stream=None) -> None:
-    """Contiguous M-grouped GEMM; rows with m_indices == -1 are not written."""
+    """Contiguous M-grouped GEMM; rows with m_indices == -1 are not written.  E4M3
+    operands; float8_e5m2 tensors are taken as E5M2 (see the _fmt call)."""
+    dg_m_grouped_gemm_fp8_contiguous_fmt(a, sa, b, sb, d, m_indices, None, None, stream)
+
+
+def dg_m_grouped_gemm_fp8_contiguous_fmt(a, sa, b, sb, d, m_indices, a_fmt=None, b_fmt=None, stream=None) -> None:
+    """The contiguous M-grouped GEMM with each operand E4M3 or E5M2 (as dg_gemm_fp8_nt_fmt)."""
     import torch
     m_total, k = a.shape
     g, n, _ = b.shape
-    pa = _dev(a, "a", _fp8_types(), 2)
+    pa = _dev(a, "a", _fp8_any_types(), 2)
     psa = _dev(sa, "sa", _f32(), 2)
-    pb = _dev(b, "b", _fp8_types(), 3)
+    pb = _dev(b, "b", _fp8_any_types(), 3)
     psb = _dev(sb, "sb", _f32(), 3)
     pd = _dev(d, "d", _bf16_types(), 2)
     pmi = _dev(m_indices, "m_indices", (torch.int32,), 1)
+    fa, fb = _fmt_of(a, a_fmt), _fmt_of(b, b_fmt)
     for t, nm in ((a, "a"), (b, "b"), (sb, "sb"), (d, "d"), (m_indices, "m_indices")):
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
@@ -213,22 +224,29 @@ def dg_m_grouped_gemm_fp8_contiguous(a, sa, b, sb, d, m_indices, stream=None) ->
         raise ValueError("shape mismatch")
     if tuple(sb.shape) != (g, -(-n // 128), -(-k // 128)) or sa.shape[0] != -(-k // 128):
         raise ValueError("scale shape mismatch")
-    _check(load_library().dg_m_grouped_gemm_fp8_contiguous(pa, psa, sa.stride(0), pb, psb, pd, pmi,
-                                                           m_total, n, k, g, _stream(stream)),
-           "dg_m_grouped_gemm_fp8_contiguous")
+    _check(load_library().dg_m_grouped_gemm_fp8_contiguous_fmt(pa, psa, sa.stride(0), pb, psb, pd, pmi,
+                                                               m_total, n, k, g, fa, fb, _stream(stream)),
+           "dg_m_grouped_gemm_fp8_contiguous_fmt")
 
 
 def dg_m_grouped_gemm_fp8_masked(a, sa, b, sb, d, masked_m, stream=None) -> None:
-    """Masked M-grouped GEMM; rows >= masked_m[g] of d are never written."""
+    """Masked M-grouped GEMM; rows >= masked_m[g] of d are never written.  E4M3
+    operands; float8_e5m2 tensors are taken as E5M2 (see the _fmt call)."""
+    dg_m_grouped_gemm_fp8_masked_fmt(a, sa, b, sb, d, masked_m, None, None, stream)
+
+
+def dg_m_grouped_gemm_fp8_masked_fmt(a, sa, b, sb, d, masked_m, a_fmt=None, b_fmt=None, stream=None) -> None:
+    """The masked M-grouped GEMM with each operand E4M3 or E5M2 (as dg_gemm_fp8_nt_fmt)."""
     import torch
     g, max_m, k = a.shape
     n = b.shape[1]
-    pa = _dev(a, "a", _fp8_types(), 3)
+    pa = _dev(a, "a", _fp8_any_types(), 3)
     psa = _dev(sa, "sa", _f32(), 3)
-    pb = _dev(b, "b", _fp8_types(), 3)
+    pb = _dev(b, "b", _fp8_any_types(), 3)
     psb = _dev(sb, "sb", _f32(), 3)
     pd = _dev(d, "d", _bf16_types(), 3)
     pmm = _dev(masked_m, "masked_m", (torch.int32,), 1)
+    fa, fb = _fmt_of(a, a_fmt), _fmt_of(b, b_fmt)
     for t, nm in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb"), (d, "d"), (masked_m, "masked_m")):
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
@@ -236,9 +254,9 @@ def dg_m_grouped_gemm_fp8_masked(a, sa, b, sb, d, masked_m, stream=None) -> None
         raise ValueError("shape mismatch")
     if tuple(sb.shape) != (g, -(-n // 128), -(-k // 128)) or sa.shape[:2] != (g, -(-k // 128)):
         raise ValueError("scale shape mismatch")
-    _check(load_library().dg_m_grouped_gemm_fp8_masked(pa, psa, sa.shape[2], pb, psb, pd, pmm,
-                                                       g, max_m, n, k, _stream(stream)),
-           "dg_m_grouped_gemm_fp8_masked")
+    _check(load_library().dg_m_grouped_gemm_fp8_masked_fmt(pa, psa, sa.shape[2], pb, psb, pd, pmm,
+                                                           g, max_m, n, k, fa, fb, _stream(stream)),
+           "dg_m_grouped_gemm_fp8_masked_fmt")
 
 
 def _quant_args(x, q, name):
@@ -319,5 +337,6 @@ __all__ = [
     "DGError", "load_library", "status_string", "dg_status_string",
     "dg_get_m_alignment", "dg_set_num_cus", "dg_get_num_cus",
     "dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "DG_FMT_E4M3", "DG_FMT_E5M2", "dg_m_grouped_gemm_fp8_contiguous", "dg_m_grouped_gemm_fp8_masked",
+    "dg_m_grouped_gemm_fp8_contiguous_fmt", "dg_m_grouped_gemm_fp8_masked_fmt",
     "dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_set_kernel_config", "dg_kernel_config_info", "dg_plan_tiles", "dg_describe_launch",
 ]

@@ -99,6 +99,11 @@ int effective_cus(int device_cus) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool valid_fmt(int f) { return f == DG_FMT_E4M3 || f == DG_FMT_E5M2; }
+
+// GemmParams::fmt: bit 0 = A is E5M2, bit 1 = B is E5M2
+int fmt_bits(int a_fmt, int b_fmt) { return (a_fmt == DG_FMT_E5M2 ? 1 : 0) | (b_fmt == DG_FMT_E5M2 ? 2 : 0); }
+
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 // Planner order: the smaller estimated makespan (waves x per-tile work); on a tie
@@ -375,8 +380,7 @@ int dg_describe_launch(int layout, int m, int n, int k, int num_groups, int num_
 
 int dg_gemm_fp8_nt_fmt(const void* a, long lda, const float* sa, long ld_sa, const void* b, long ldb, const float* sb,
                        void* d, long ldd, int m, int n, int k, int a_fmt, int b_fmt, void* stream) {
-    if ((a_fmt != DG_FMT_E4M3 && a_fmt != DG_FMT_E5M2) || (b_fmt != DG_FMT_E4M3 && b_fmt != DG_FMT_E5M2))
-        return DG_ERR_INVALID_ARG;
+    if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt)) return DG_ERR_INVALID_ARG;
     int st = check_common(n, k, b, sb, d);
     if (st != DG_OK) return st;
     if (m < 0) return DG_ERR_INVALID_ARG;
@@ -401,7 +405,7 @@ int dg_gemm_fp8_nt_fmt(const void* a, long lda, const float* sa, long ld_sa, con
     p.kblocks = k / kKBlock;
     p.nblocks = (int)ceil_div(n, kKBlock);
     p.num_groups = 1;
-    p.fmt = (a_fmt == DG_FMT_E5M2 ? 1 : 0) | (b_fmt == DG_FMT_E5M2 ? 2 : 0);
+    p.fmt = fmt_bits(a_fmt, b_fmt);
     return launch(dg::kDense, p, m, m, static_cast<hipStream_t>(stream), 0, nullptr);
 }
 
@@ -410,9 +414,10 @@ int dg_gemm_fp8_nt(const void* a, long lda, const float* sa, long ld_sa, const v
     return dg_gemm_fp8_nt_fmt(a, lda, sa, ld_sa, b, ldb, sb, d, ldd, m, n, k, DG_FMT_E4M3, DG_FMT_E4M3, stream);
 }
 
-int dg_m_grouped_gemm_fp8_contiguous(const void* a, const float* sa, long ld_sa, const void* b, const float* sb,
-                                     void* d, const int* m_indices, int m_total, int n, int k, int num_groups,
-                                     void* stream) {
+int dg_m_grouped_gemm_fp8_contiguous_fmt(const void* a, const float* sa, long ld_sa, const void* b, const float* sb,
+                                         void* d, const int* m_indices, int m_total, int n, int k, int num_groups,
+                                         int a_fmt, int b_fmt, void* stream) {
+    if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt)) return DG_ERR_INVALID_ARG;
     int st = check_common(n, k, b, sb, d);
     if (st != DG_OK) return st;
     if (m_total < 0 || num_groups < 1) return DG_ERR_INVALID_ARG;
@@ -441,12 +446,21 @@ int dg_m_grouped_gemm_fp8_contiguous(const void* a, const float* sa, long ld_sa,
     p.kblocks = k / kKBlock;
     p.nblocks = (int)ceil_div(n, kKBlock);
     p.num_groups = num_groups;
+    p.fmt = fmt_bits(a_fmt, b_fmt);
     return launch(dg::kContiguous, p, m_total, m_total, static_cast<hipStream_t>(stream), 0, nullptr);
 }
 
-int dg_m_grouped_gemm_fp8_masked(const void* a, const float* sa, long ld_sa, const void* b, const float* sb,
-                                 void* d, const int* masked_m, int num_groups, int max_m, int n, int k,
-                                 void* stream) {
+int dg_m_grouped_gemm_fp8_contiguous(const void* a, const float* sa, long ld_sa, const void* b, const float* sb,
+                                     void* d, const int* m_indices, int m_total, int n, int k, int num_groups,
+                                     void* stream) {
+    return dg_m_grouped_gemm_fp8_contiguous_fmt(a, sa, ld_sa, b, sb, d, m_indices, m_total, n, k, num_groups,
+                                                DG_FMT_E4M3, DG_FMT_E4M3, stream);
+}
+
+int dg_m_grouped_gemm_fp8_masked_fmt(const void* a, const float* sa, long ld_sa, const void* b, const float* sb,
+                                     void* d, const int* masked_m, int num_groups, int max_m, int n, int k,
+                                     int a_fmt, int b_fmt, void* stream) {
+    if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt)) return DG_ERR_INVALID_ARG;
     int st = check_common(n, k, b, sb, d);
     if (st != DG_OK) return st;
     if (max_m < 0 || num_groups < 1) return DG_ERR_INVALID_ARG;
@@ -478,7 +492,15 @@ int dg_m_grouped_gemm_fp8_masked(const void* a, const float* sa, long ld_sa, con
     p.kblocks = k / kKBlock;
     p.nblocks = (int)ceil_div(n, kKBlock);
     p.num_groups = num_groups;
+    p.fmt = fmt_bits(a_fmt, b_fmt);
     return launch(dg::kMasked, p, max_m, max_m, static_cast<hipStream_t>(stream), 0, nullptr);
+}
+
+int dg_m_grouped_gemm_fp8_masked(const void* a, const float* sa, long ld_sa, const void* b, const float* sb,
+                                 void* d, const int* masked_m, int num_groups, int max_m, int n, int k,
+                                 void* stream) {
+    return dg_m_grouped_gemm_fp8_masked_fmt(a, sa, ld_sa, b, sb, d, masked_m, num_groups, max_m, n, k,
+                                            DG_FMT_E4M3, DG_FMT_E4M3, stream);
 }
 
 }  // extern "C"

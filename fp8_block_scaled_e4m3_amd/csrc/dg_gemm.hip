@@ -923,15 +923,15 @@ static const KernelConfig kConfigs[] = {
     DG_CFG(5, kDense, 256, 256, 4, 2, 16, 2, 1.15, true, true),
     // contiguous (BLOCK_M = the 128-row segment alignment)
     DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false, false),
-    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false, false),
+    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false, true),
     DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95, true, false),
-    DG_CFG(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false, false),
+    DG_CFG(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false, true),
     // masked
     DG_CFG(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false, false),
-    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false, false),
+    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false, true),
     DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false, false),
     DG_CFG(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90, false, false),
-    DG_CFG(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, false),
+    DG_CFG(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, true),
 };
 
 const KernelConfig* kernel_configs(int* count) {

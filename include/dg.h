@@ -128,6 +128,22 @@ int dg_m_grouped_gemm_fp8_masked(const void* a, const float* sa, long ld_sa,
                                  int num_groups, int max_m, int n, int k,
                                  void* stream);
 
+/* The two grouped GEMMs with each operand's FP8 format chosen (DG_FMT_E4M3 or
+ * DG_FMT_E5M2 for a and for b, as in dg_gemm_fp8_nt_fmt, after the same blog
+ * section).  Everything else is exactly the call without _fmt, which is this
+ * call with two E4M3 operands.  An unknown format is DG_ERR_INVALID_ARG; E5M2
+ * operands run on a subset of the tile configurations. */
+int dg_m_grouped_gemm_fp8_contiguous_fmt(const void* a, const float* sa, long ld_sa,
+                                         const void* b, const float* sb,
+                                         void* d, const int* m_indices,
+                                         int m_total, int n, int k, int num_groups,
+                                         int a_fmt, int b_fmt, void* stream);
+int dg_m_grouped_gemm_fp8_masked_fmt(const void* a, const float* sa, long ld_sa,
+                                     const void* b, const float* sb,
+                                     void* d, const int* masked_m,
+                                     int num_groups, int max_m, int n, int k,
+                                     int a_fmt, int b_fmt, void* stream);
+
 /* Input element types of the casts below. */
 enum { DG_DTYPE_F32 = 0, DG_DTYPE_BF16 = 1 };
 

@@ -74,17 +74,31 @@ def _call_dense_fmt(lib, a_fmt, b_fmt, k=512):
                                   a_fmt, b_fmt, None)
 
 
+def _call_grouped_fmt(lib, layout, a_fmt, b_fmt, k=512):
+    P = ctypes.c_void_p
+    if layout == 1:
+        return lib.dg_m_grouped_gemm_fp8_contiguous_fmt(P(16), P(16), 128, P(16), P(16), P(16), P(16),
+                                                        128, 128, k, 2, a_fmt, b_fmt, None)
+    return lib.dg_m_grouped_gemm_fp8_masked_fmt(P(16), P(16), 128, P(16), P(16), P(16), P(16),
+                                                2, 128, 128, k, a_fmt, b_fmt, None)
+
+
 def test_format_entry_validation(lib):
-    """Unknown format codes are rejected before anything else; the E5M2 variants are
-    compiled for dense configurations only."""
+    """Unknown format codes are rejected before anything else, in every layout; every
+    layout has configurations that carry the E5M2 variants."""
     assert (dg.DG_FMT_E4M3, dg.DG_FMT_E5M2) == (0, 1)
     for fa, fb in ((2, 0), (0, -1), (7, 7)):
         assert _call_dense_fmt(lib, fa, fb) == dg.DG_ERR_INVALID_ARG
+        assert _call_grouped_fmt(lib, 1, fa, fb) == dg.DG_ERR_INVALID_ARG
+        assert _call_grouped_fmt(lib, 2, fa, fb) == dg.DG_ERR_INVALID_ARG
     for fa, fb in ((0, 1), (1, 0), (1, 1)):
         assert _call_dense_fmt(lib, fa, fb, k=500) == dg.DG_ERR_UNSUPPORTED
+        assert _call_grouped_fmt(lib, 1, fa, fb, k=500) == dg.DG_ERR_UNSUPPORTED
+        assert _call_grouped_fmt(lib, 2, fa, fb, k=500) == dg.DG_ERR_UNSUPPORTED
     cfgs = dg.dg_kernel_config_info()
-    assert any(c["all_formats"] for c in cfgs if c["layout"] == 0)
-    assert not any(c["all_formats"] for c in cfgs if c["layout"] != 0)
+    for layout in (0, 1, 2):
+        assert any(c["all_formats"] for c in cfgs if c["layout"] == layout)
+        assert not all(c["all_formats"] for c in cfgs if c["layout"] == layout)
 
 
 def test_dense_validation_before_any_device_work(lib):

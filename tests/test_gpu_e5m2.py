@@ -1,10 +1,10 @@
-"""GPU parity for the dense GEMM with E5M2 operands (either side, or both).
+"""GPU parity for the GEMMs with E5M2 operands (either side, or both).
 
 The blog's FP8 section lets each operand be E4M3 or E5M2.  Every combination is
 compared with the oracle element by element on small and ragged shapes in each
-tile configuration that carries the E5M2 variants, through the planner, and on a
-larger shape on sampled rows; the E4M3/E4M3 case of the same entry point must be
-bit-identical to the plain dense entry point.
+tile configuration that carries the E5M2 variants (dense, contiguous and masked
+layouts), through the planner, and on a larger dense shape on sampled rows; the
+E4M3/E4M3 case of each _fmt entry point must be bit-identical to the plain one.
 """
 import numpy as np
 import pytest
@@ -27,8 +27,8 @@ def gpu():
     dg.dg_set_num_cus(0)
 
 
-def fmt_configs():
-    return [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and c["all_formats"]]
+def fmt_configs(layout=0):
+    return [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == layout and c["all_formats"]]
 
 
 def run_fmt(dd, cfg=-1, pad_cols=16):
@@ -55,7 +55,7 @@ def oracle_fmt(orc, dd, rows=None):
 
 
 def test_format_configs_exist():
-    assert len(fmt_configs()) >= 2
+    assert len(fmt_configs(0)) >= 2 and len(fmt_configs(1)) >= 2 and len(fmt_configs(2)) >= 2
 
 
 @pytest.mark.parametrize("a_fmt,b_fmt", COMBOS)
@@ -140,3 +140,99 @@ def test_forced_config_without_formats_is_unsupported():
     assert e.value.status == dg.DG_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.count_nonzero(d).item() == 0
+
+
+# --------------------------------------------------------------------------- grouped layouts
+def run_contiguous_fmt(cd, cfg=-1, a_fmt=None, b_fmt=None):
+    import torch
+    dv = upload(cd)
+    out = sentinel_like((cd["m_total"], cd["n"]))
+    dg.dg_set_kernel_config(cfg)
+    try:
+        dg.dg_m_grouped_gemm_fp8_contiguous_fmt(dv["a"], dv["sa"], dv["b"], dv["sb"], out, dv["m_indices"],
+                                                a_fmt=a_fmt or cd["a_fmt"], b_fmt=b_fmt or cd["b_fmt"])
+        torch.cuda.synchronize()
+    finally:
+        dg.dg_set_kernel_config(-1)
+    return bits(out)
+
+
+def run_masked_fmt(md, cfg=-1, a_fmt=None, b_fmt=None):
+    import torch
+    dv = upload(md)
+    out = sentinel_like((md["groups"], md["max_m"], md["n"]))
+    dg.dg_set_kernel_config(cfg)
+    try:
+        dg.dg_m_grouped_gemm_fp8_masked_fmt(dv["a"], dv["sa"], dv["b"], dv["sb"], out, dv["masked_m"],
+                                            a_fmt=a_fmt or md["a_fmt"], b_fmt=b_fmt or md["b_fmt"])
+        torch.cuda.synchronize()
+    finally:
+        dg.dg_set_kernel_config(-1)
+    return bits(out)
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", COMBOS)
+def test_e5m2_contiguous(orc, a_fmt, b_fmt):
+    counts = [130, 0, 3, 257]
+    cd = W.make_contiguous(counts, n=208, k=384, seed=31, a_fmt=a_fmt, b_fmt=b_fmt)
+    sentinel = np.full((cd["m_total"], 208), W.SENTINEL_BF16, np.uint16)
+    ref = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], cd["m_indices"], d_init=sentinel,
+                                   a_fmt=a_fmt, b_fmt=b_fmt)
+    valid = cd["m_indices"] >= 0
+    outs = []
+    for cfg in [-1] + fmt_configs(1):
+        say(f"contiguous {a_fmt}x{b_fmt} counts={counts} n=208 k=384 cfg={cfg}")
+        out = run_contiguous_fmt(cd, cfg)
+        check_values(out[valid], ref[valid], f"contiguous {a_fmt}x{b_fmt} cfg{cfg}")
+        assert np.all(out[~valid] == W.SENTINEL_BF16), "a padding row was written"
+        outs.append(out)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", COMBOS)
+def test_e5m2_masked(orc, a_fmt, b_fmt):
+    mm = [0, 1, 70, 256, 129]
+    md = W.make_masked(5, 256, 208, 384, seed=32, masked_m=mm, a_fmt=a_fmt, b_fmt=b_fmt)
+    sentinel = np.full((5, 256, 208), W.SENTINEL_BF16, np.uint16)
+    ref = orc.m_grouped_masked(md["a"], md["sa"], md["b"], md["sb"], md["masked_m"], d_init=sentinel,
+                               a_fmt=a_fmt, b_fmt=b_fmt)
+    outs = []
+    for cfg in [-1] + fmt_configs(2):
+        say(f"masked {a_fmt}x{b_fmt} masked_m={mm} n=208 k=384 cfg={cfg}")
+        out = run_masked_fmt(md, cfg)
+        for g, c in enumerate(mm):
+            assert np.all(out[g, c:] == W.SENTINEL_BF16), f"group {g}: a row >= masked_m was written"
+            if c:
+                check_values(out[g, :c], ref[g, :c], f"masked {a_fmt}x{b_fmt} cfg{cfg} group {g}")
+        outs.append(out)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_grouped_e4m3_pair_matches_plain_entries():
+    import torch
+    cd = W.make_contiguous([100, 40], n=96, k=256, seed=33)
+    dv = upload(cd)
+    o0, o1 = sentinel_like((cd["m_total"], 96)), sentinel_like((cd["m_total"], 96))
+    dg.dg_m_grouped_gemm_fp8_contiguous(dv["a"], dv["sa"], dv["b"], dv["sb"], o0, dv["m_indices"])
+    dg.dg_m_grouped_gemm_fp8_contiguous_fmt(dv["a"], dv["sa"], dv["b"], dv["sb"], o1, dv["m_indices"],
+                                            a_fmt="e4m3", b_fmt="e4m3")
+    md = W.make_masked(3, 64, 96, 256, seed=34, masked_m=[64, 0, 9])
+    mv = upload(md)
+    p0, p1 = sentinel_like((3, 64, 96)), sentinel_like((3, 64, 96))
+    dg.dg_m_grouped_gemm_fp8_masked(mv["a"], mv["sa"], mv["b"], mv["sb"], p0, mv["masked_m"])
+    dg.dg_m_grouped_gemm_fp8_masked_fmt(mv["a"], mv["sa"], mv["b"], mv["sb"], p1, mv["masked_m"],
+                                        a_fmt="e4m3", b_fmt="e4m3")
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o0), bits(o1))
+    assert np.array_equal(bits(p0), bits(p1))
+
+
+def test_grouped_forced_config_without_formats_is_unsupported():
+    plain = [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 2 and not c["all_formats"]]
+    assert plain
+    md = W.make_masked(2, 64, 96, 256, seed=35, masked_m=[64, 9], a_fmt="e5m2", b_fmt="e5m2")
+    with pytest.raises(dg.DGError) as e:
+        run_masked_fmt(md, plain[0])
+    assert e.value.status == dg.DG_ERR_UNSUPPORTED
