@@ -101,6 +101,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_fmt(int f) { return f == DG_FMT_E4M3 || f == DG_FMT_E5M2; }
 
+// The kernels address a tile's operands through 32-bit buffer offsets from the
+// tile's first row: up to 256 rows of A or B (row stride lda / ldb bytes) plus the
+// K offset, and the A scales of all K blocks (k/128 rows of ld_sa floats).  Sizes
+// whose offsets would not fit are refused rather than wrapped.
+bool offsets_fit(long lda, long ldb, long ld_sa, int k) {
+    const long lim = 0xFFFFFFFFl;
+    return 256 * lda + k <= lim && 256 * ldb + k <= lim && (long)(k / kKBlock) * ld_sa * 4 + 4096 <= lim;
+}
+
 // GemmParams::fmt: bit 0 = A is E5M2, bit 1 = B is E5M2
 int fmt_bits(int a_fmt, int b_fmt) { return (a_fmt == DG_FMT_E5M2 ? 1 : 0) | (b_fmt == DG_FMT_E5M2 ? 2 : 0); }
 
@@ -189,13 +198,10 @@ int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_
     const int per_cu = dev ? dev->occ[ci] : 1;
 
     p.tiles_n = (int)ceil_div(p.n, c.bn);
-    if (layout == dg::kMasked) {
-        p.tiles_m = (int)ceil_div(p.rows, c.bm);
-        p.num_tiles = p.num_groups * p.tiles_m * p.tiles_n;
-    } else {
-        p.tiles_m = (int)ceil_div(p.rows, c.bm);
-        p.num_tiles = p.tiles_m * p.tiles_n;
-    }
+    p.tiles_m = (int)ceil_div(p.rows, c.bm);
+    const long tiles = (long)p.tiles_m * p.tiles_n * (layout == dg::kMasked ? p.num_groups : 1);
+    if (tiles > INT_MAX / 2) return DG_ERR_UNSUPPORTED;   // tile indices are 32-bit on the device
+    p.num_tiles = (int)tiles;
     long slots = (long)units * per_cu;
     long grid = p.num_tiles < slots ? p.num_tiles : slots;
     if (grid < 1) grid = 1;
@@ -388,7 +394,7 @@ int dg_gemm_fp8_nt_fmt(const void* a, long lda, const float* sa, long ld_sa, con
     if (!a || !sa) return DG_ERR_INVALID_ARG;
     if (lda < k || ldb < k || ldd < n || ld_sa < m) return DG_ERR_INVALID_ARG;
     if (!aligned16(a) || !aligned16(sa) || lda % 16 || ldb % 16 || ldd % 8 || ld_sa % 4) return DG_ERR_MISALIGNED;
-    if ((long)m * lda > LONG_MAX / 2) return DG_ERR_UNSUPPORTED;
+    if ((long)m * lda > LONG_MAX / 2 || !offsets_fit(lda, ldb, ld_sa, k)) return DG_ERR_UNSUPPORTED;
     GemmParams p{};
     p.a = static_cast<const uint8_t*>(a);
     p.lda = lda;
@@ -427,6 +433,7 @@ int dg_m_grouped_gemm_fp8_contiguous_fmt(const void* a, const float* sa, long ld
     if (ld_sa < m_total) return DG_ERR_INVALID_ARG;
     if (!aligned16(a) || !aligned16(sa) || k % 16 || ld_sa % 4 || (reinterpret_cast<uintptr_t>(m_indices) & 3u))
         return DG_ERR_MISALIGNED;
+    if (!offsets_fit(k, k, ld_sa, k)) return DG_ERR_UNSUPPORTED;
     GemmParams p{};
     p.a = static_cast<const uint8_t*>(a);
     p.lda = k;
@@ -470,6 +477,7 @@ int dg_m_grouped_gemm_fp8_masked_fmt(const void* a, const float* sa, long ld_sa,
     if (ld_sa < max_m) return DG_ERR_INVALID_ARG;
     if (!aligned16(a) || !aligned16(sa) || k % 16 || ld_sa % 4 || (reinterpret_cast<uintptr_t>(masked_m) & 3u))
         return DG_ERR_MISALIGNED;
+    if (!offsets_fit(k, k, ld_sa, k)) return DG_ERR_UNSUPPORTED;
     GemmParams p{};
     p.a = static_cast<const uint8_t*>(a);
     p.lda = k;

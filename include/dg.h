@@ -31,6 +31,10 @@
  *    DG_ERR_UNSUPPORTED); a, b, d, sa, sb 16-byte aligned; lda, ldb multiples of 16
  *    and >= K; ldd a multiple of 8 and >= N; ld_sa a multiple of 4 and >= the row
  *    count (else DG_ERR_MISALIGNED / DG_ERR_INVALID_ARG).
+ *  - Size limits (else DG_ERR_UNSUPPORTED): 256 * lda + K and 256 * ldb + K below
+ *    2^32 bytes, (K / 128) * ld_sa * 4 + 4096 below 2^32 bytes (for the grouped
+ *    layouts lda = ldb = K), and fewer than 2^30 output tiles; the kernels address
+ *    each tile's operands through 32-bit offsets from the tile's first row.
  *  - M == 0 (or all masked_m == 0) is a valid no-op.
  *  - Calls on distinct streams may run concurrently; the only library state is the
  *    CU cap (dg_set_num_cus) and a per-device property cache.
@@ -45,7 +49,7 @@ extern "C" {
 enum {
     DG_OK = 0,
     DG_ERR_INVALID_ARG = -1,   /* null pointer, negative size, leading dimension too small */
-    DG_ERR_UNSUPPORTED = -2,   /* shape outside what the kernels handle (K % 128, N % 16) */
+    DG_ERR_UNSUPPORTED = -2,   /* shape outside what the kernels handle (K % 128, N % 16, size limits) */
     DG_ERR_MISALIGNED = -3,    /* pointer or leading dimension alignment */
     DG_ERR_HIP = -4            /* a HIP runtime call or the kernel launch failed */
 };

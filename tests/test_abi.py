@@ -116,6 +116,23 @@ def test_dense_validation_before_any_device_work(lib):
     assert _call_dense(lib, m=0) == dg.DG_OK           # empty problem: no-op, no device needed
 
 
+def test_size_limits_of_32bit_offsets(lib):
+    """Sizes whose per-tile offsets would not fit in 32 bits are refused on the host
+    (before any device work), in every layout."""
+    P = ctypes.c_void_p
+    k = 7168
+    big_ld = (0xFFFFFFFF - k) // 256 + 16          # 256 * ld + k just past 2^32
+    assert _call_dense(lib, lda=big_ld - big_ld % 16, ldb=k, k=k, ld_sa=128) == dg.DG_ERR_UNSUPPORTED
+    assert _call_dense(lib, lda=k, ldb=big_ld - big_ld % 16, k=k, ld_sa=128) == dg.DG_ERR_UNSUPPORTED
+    # A scales: (k/128) * ld_sa * 4 past 2^32 (rows that would fit in HBM at small N)
+    rows = (0xFFFFFFFF // (4 * (k // 128))) // 4 * 4 + 4
+    assert _call_dense(lib, m=rows, lda=k, ldb=k, ld_sa=rows, k=k) == dg.DG_ERR_UNSUPPORTED
+    assert lib.dg_m_grouped_gemm_fp8_contiguous(P(16), P(16), rows + 124, P(16), P(16), P(16), P(16),
+                                                (rows // 128 + 1) * 128, 128, k, 2, None) == dg.DG_ERR_UNSUPPORTED
+    assert lib.dg_m_grouped_gemm_fp8_masked(P(16), P(16), rows, P(16), P(16), P(16), P(16),
+                                            2, rows, 128, k, None) == dg.DG_ERR_UNSUPPORTED
+
+
 def test_grouped_validation(lib):
     P = ctypes.c_void_p
     c = lib.dg_m_grouped_gemm_fp8_contiguous
