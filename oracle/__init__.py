@@ -78,6 +78,12 @@ def _load():
     lib.orc_quantize_rows_1x128.restype = None
     lib.orc_quantize_blocks_128x128.argtypes = [P, L, I, I, P, L, P]
     lib.orc_quantize_blocks_128x128.restype = None
+    lib.orc_e5m2_encode.argtypes = [ctypes.c_double]
+    lib.orc_e5m2_encode.restype = ctypes.c_uint8
+    lib.orc_quantize_rows_1x128_fmt.argtypes = [P, L, I, I, P, L, P, L, I]
+    lib.orc_quantize_rows_1x128_fmt.restype = None
+    lib.orc_quantize_blocks_128x128_fmt.argtypes = [P, L, I, I, P, L, P, I]
+    lib.orc_quantize_blocks_128x128_fmt.restype = None
     lib.orc_available_cores.argtypes = []
     lib.orc_available_cores.restype = I
     lib.orc_gemm_fp8_nt.argtypes = [P, L, P, L, P, L, P, P, L, P, I, I, I, I]
@@ -133,6 +139,10 @@ def e4m3_encode(x: float) -> int:
     return int(_load().orc_e4m3_encode(float(x)))
 
 
+def e5m2_encode(x: float) -> int:
+    return int(_load().orc_e5m2_encode(float(x)))
+
+
 def bf16_encode(x: float) -> int:
     return int(_load().orc_bf16_encode(float(x)))
 
@@ -150,24 +160,32 @@ def block_dot_fmt(a, b, a_fmt="e4m3", b_fmt="e4m3") -> float:
     return float(_load().orc_block_dot_fmt(_ptr(a), _ptr(b), int(a.size), FORMATS[a_fmt], FORMATS[b_fmt]))
 
 
-def quantize_rows_1x128(x):
-    """fp32 [m, k] -> (E4M3 bytes [m, k], sa fp32 [ceil(k/128), m]) (MN-major scales)."""
+def quantize_rows_1x128(x, fmt="e4m3"):
+    """fp32 [m, k] -> (FP8 bytes [m, k], sa fp32 [ceil(k/128), m]) (MN-major scales);
+    fmt "e4m3" (scale amax/448) or "e5m2" (scale amax/57344)."""
     x = _f32(x)
     m, k = x.shape
     kb = -(-k // KBLOCK)
     q = np.empty((m, k), dtype=np.uint8)
     sa = np.empty((kb, m), dtype=np.float32)
-    _load().orc_quantize_rows_1x128(_ptr(x), k, m, k, _ptr(q), k, _ptr(sa), m)
+    if fmt == "e4m3":
+        _load().orc_quantize_rows_1x128(_ptr(x), k, m, k, _ptr(q), k, _ptr(sa), m)
+    else:
+        _load().orc_quantize_rows_1x128_fmt(_ptr(x), k, m, k, _ptr(q), k, _ptr(sa), m, FORMATS[fmt])
     return q, sa
 
 
-def quantize_blocks_128x128(x):
-    """fp32 [n, k] -> (E4M3 bytes [n, k], sb fp32 [ceil(n/128), ceil(k/128)])."""
+def quantize_blocks_128x128(x, fmt="e4m3"):
+    """fp32 [n, k] -> (FP8 bytes [n, k], sb fp32 [ceil(n/128), ceil(k/128)]); fmt as
+    in quantize_rows_1x128."""
     x = _f32(x)
     n, k = x.shape
     q = np.empty((n, k), dtype=np.uint8)
     sb = np.empty((-(-n // KBLOCK), -(-k // KBLOCK)), dtype=np.float32)
-    _load().orc_quantize_blocks_128x128(_ptr(x), k, n, k, _ptr(q), k, _ptr(sb))
+    if fmt == "e4m3":
+        _load().orc_quantize_blocks_128x128(_ptr(x), k, n, k, _ptr(q), k, _ptr(sb))
+    else:
+        _load().orc_quantize_blocks_128x128_fmt(_ptr(x), k, n, k, _ptr(q), k, _ptr(sb), FORMATS[fmt])
     return q, sb
 
 

@@ -149,6 +149,33 @@ uint8_t orc_e4m3_encode(double x)
 }
 
 /* ------------------------------------------------------------------------- */
+/* E5M2 encode: round to nearest, ties to even mantissa, saturating to       */
+/* +-57344 (the format's largest finite value; the same reading as for       */
+/* E4M3: a scaled value never lands on an infinity).  NaN in gives 0x7F.     */
+/* Exponent bias 15, 2 stored mantissa bits, subnormal quantum 2^-16.        */
+/* ------------------------------------------------------------------------- */
+uint8_t orc_e5m2_encode(double x)
+{
+    unsigned sign;
+    double a, q, n;
+    int e, E;
+    if (isnan(x)) return 0x7Fu;
+    sign = signbit(x) ? 0x80u : 0u;
+    a = fabs(x);
+    if (a >= 57344.0) return (uint8_t)(sign | 0x7Bu);
+    if (a == 0.0) return (uint8_t)sign;
+    frexp(a, &e);               /* a = frac * 2^e, frac in [0.5, 1) */
+    E = e - 1;                  /* floor(log2(a)) */
+    if (E < -14) E = -14;       /* below the smallest normal the quantum stays 2^-16 */
+    q = ldexp(1.0, E - 2);      /* 2 stored mantissa bits */
+    n = nearbyint(a / q);       /* exact division by a power of two; RNE (default mode) */
+    if (n < 4.0) return (uint8_t)(sign | (unsigned)n);          /* subnormal (E == -14) */
+    if (n >= 8.0) { n = 4.0; E += 1; }                           /* carry into exponent */
+    if (E + 15 > 30) return (uint8_t)(sign | 0x7Bu);            /* cannot happen below 57344 */
+    return (uint8_t)(sign | ((unsigned)(E + 15) << 2) | (unsigned)(n - 4.0));
+}
+
+/* ------------------------------------------------------------------------- */
 /* BF16 encode from double: round to nearest, ties to even, one rounding.    */
 /* 8 significant bits; below 2^-126 the quantum is fixed at 2^-133           */
 /* (subnormals); results of magnitude >= 2^128 after rounding become inf;    */
@@ -178,25 +205,37 @@ uint16_t orc_bf16_encode(double x)
 
 /* ------------------------------------------------------------------------- */
 /* Quantisers (input preparation; the pages leave the cast to a prior        */
-/* kernel).  scale = fp32(amax / 448); q = E4M3_RNE(clamp(fp32(x / scale)))  */
-/* with amax == 0 giving scale 1.  Arithmetic is fp32, as a cast kernel      */
-/* working on fp32 input would do it.                                        */
+/* kernel).  scale = fp32(amax / FMAX); q = FP8_RNE(clamp(fp32(x / scale)))  */
+/* with amax == 0 giving scale 1, FMAX = 448 for E4M3 (fmt 0) and 57344 for  */
+/* E5M2 (fmt 1).  Arithmetic is fp32, as a cast kernel working on fp32 input */
+/* would do it.                                                              */
 /* ------------------------------------------------------------------------- */
-static float block_scale(float amax)
+static float block_scale(float amax, int fmt)
 {
-    volatile float s = amax / 448.0f;
+    volatile float s = amax / (fmt ? 57344.0f : 448.0f);
     return amax == 0.0f ? 1.0f : s;
 }
 
-static uint8_t quant_one(float x, float s)
+static uint8_t quant_one(float x, float s, int fmt)
 {
     volatile float y = x / s;
-    return orc_e4m3_encode((double)y);
+    return fmt ? orc_e5m2_encode((double)y) : orc_e4m3_encode((double)y);
 }
+
+void orc_quantize_rows_1x128_fmt(const float* x, long ldx, int m, int k,
+                                 uint8_t* q, long ldq, float* sa, long ld_sa, int fmt);
+void orc_quantize_blocks_128x128_fmt(const float* x, long ldx, int n, int k,
+                                     uint8_t* q, long ldq, float* sb, int fmt);
 
 /* A-side: one scale per (row, 128-wide K block), stored sa[kb * ld_sa + m]. */
 void orc_quantize_rows_1x128(const float* x, long ldx, int m, int k,
                              uint8_t* q, long ldq, float* sa, long ld_sa)
+{
+    orc_quantize_rows_1x128_fmt(x, ldx, m, k, q, ldq, sa, ld_sa, 0);
+}
+
+void orc_quantize_rows_1x128_fmt(const float* x, long ldx, int m, int k,
+                                 uint8_t* q, long ldq, float* sa, long ld_sa, int fmt)
 {
     int kbn = (k + ORC_KBLOCK - 1) / ORC_KBLOCK;
     for (int i = 0; i < m; ++i) {
@@ -207,10 +246,10 @@ void orc_quantize_rows_1x128(const float* x, long ldx, int m, int k,
                 float v = fabsf(x[(long)i * ldx + kk]);
                 if (v > amax) amax = v;
             }
-            s = block_scale(amax);
+            s = block_scale(amax, fmt);
             sa[(long)kb * ld_sa + i] = s;
             for (int kk = k0; kk < k1; ++kk)
-                q[(long)i * ldq + kk] = quant_one(x[(long)i * ldx + kk], s);
+                q[(long)i * ldq + kk] = quant_one(x[(long)i * ldx + kk], s, fmt);
         }
     }
 }
@@ -218,6 +257,12 @@ void orc_quantize_rows_1x128(const float* x, long ldx, int m, int k,
 /* B-side: one scale per (128-row N block, 128-wide K block), sb[nb * Kb + kb]. */
 void orc_quantize_blocks_128x128(const float* x, long ldx, int n, int k,
                                  uint8_t* q, long ldq, float* sb)
+{
+    orc_quantize_blocks_128x128_fmt(x, ldx, n, k, q, ldq, sb, 0);
+}
+
+void orc_quantize_blocks_128x128_fmt(const float* x, long ldx, int n, int k,
+                                     uint8_t* q, long ldq, float* sb, int fmt)
 {
     int kbn = (k + ORC_KBLOCK - 1) / ORC_KBLOCK;
     int nbn = (n + ORC_KBLOCK - 1) / ORC_KBLOCK;
@@ -231,11 +276,11 @@ void orc_quantize_blocks_128x128(const float* x, long ldx, int n, int k,
                     float v = fabsf(x[(long)r * ldx + kk]);
                     if (v > amax) amax = v;
                 }
-            s = block_scale(amax);
+            s = block_scale(amax, fmt);
             sb[(long)nb * kbn + kb] = s;
             for (int r = n0; r < n1; ++r)
                 for (int kk = k0; kk < k1; ++kk)
-                    q[(long)r * ldq + kk] = quant_one(x[(long)r * ldx + kk], s);
+                    q[(long)r * ldq + kk] = quant_one(x[(long)r * ldx + kk], s, fmt);
         }
     }
 }

@@ -202,6 +202,72 @@ def test_e5m2_table_matches_torch(orc):
     assert np.array_equal(dec[ok], ref[ok])
 
 
+# --------------------------------------------------------------------------- E5M2 encode
+@pytest.mark.parametrize("x,byte", [
+    (1.0, 0x3C),
+    (1.125, 0x3C),                 # tie between 1.0 and 1.25 -> even mantissa 1.0
+    (1.375, 0x3E),                 # tie between 1.25 and 1.5 -> 1.5
+    (1.125 + 2.0 ** -20, 0x3D),
+    (2.0 ** -16, 0x01),            # smallest subnormal
+    (2.0 ** -17, 0x00),            # half of it -> 0 (even)
+    (3 * 2.0 ** -17, 0x02),        # tie between 2^-16 and 2^-15 -> 2^-15
+    (7 * 2.0 ** -17, 0x04),        # 3.5 * 2^-16 rounds up into the smallest normal 2^-14
+    (57344.0, 0x7B),               # largest finite
+    (60000.0, 0x7B),               # saturates at 57344
+    (1e30, 0x7B),
+    (float("inf"), 0x7B),
+    (-60000.0, 0xFB),
+    (-0.0, 0x80),
+    (0.0, 0x00),
+    (float("nan"), 0x7F),
+])
+def test_e5m2_encode_closed_forms(orc, x, byte):
+    assert orc.e5m2_encode(x) == byte
+
+
+def test_e5m2_encode_roundtrip_and_torch(orc):
+    """Every finite byte encodes back to itself; on finite values within the range,
+    including every midpoint between neighbouring E5M2 values and the fp32 values
+    next to it, the encoder equals torch's float32 -> float8_e5m2 cast."""
+    dec = torch_e5m2_values()
+    fin = [b for b in range(256) if np.isfinite(dec[b])]
+    for b in fin:
+        assert orc.e5m2_encode(dec[b]) == b
+    pos = np.unique(np.abs(dec[fin]))
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    rng = np.random.default_rng(9)
+    vals = np.concatenate([
+        mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf)),
+        rng.standard_normal(3000).astype(np.float32) * 5000,
+        rng.uniform(-2.0 ** -13, 2.0 ** -13, 2000).astype(np.float32),   # subnormal range
+    ]).astype(np.float32)
+    vals = np.concatenate([vals, -vals])
+    vals = vals[np.abs(vals) <= 57344.0]
+    ref = torch.from_numpy(vals).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    got = np.array([orc.e5m2_encode(float(v)) for v in vals], np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_e5m2_quantisers_match_generator(orc):
+    """E5M2 casts: the oracle's quantiser and the generator's torch-based cast agree bit
+    for bit, and every non-zero block reaches +-57344 at its amax."""
+    x = np.random.default_rng(4).standard_normal((261, 700)).astype(np.float32)
+    x[7, 128:256] = 0.0
+    q1, s1 = W.quant_rows_1x128(x, "e5m2")
+    qa, s2 = orc.quantize_rows_1x128(x, "e5m2")
+    assert np.array_equal(q1, qa) and np.array_equal(s1[:, :261], s2)
+    q1, s1 = W.quant_blocks_128x128(x, "e5m2")
+    q2, s2 = orc.quantize_blocks_128x128(x, "e5m2")
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+    dec = orc.e5m2_decode_table()
+    blk = np.abs(dec[qa[:, :640]].reshape(261, 5, 128)).max(axis=2)
+    assert np.all((blk == 57344.0) | (blk == 0.0)) and (blk == 0.0).sum() == 1
+    blk = np.abs(dec[q2[:256, :640]].reshape(2, 128, 5, 128)).max(axis=(1, 3))
+    assert np.all(blk == 57344.0)
+    # the same bytes through the format path equal the plain path for E4M3
+    assert np.array_equal(orc.quantize_rows_1x128(x, "e4m3")[0], orc.quantize_rows_1x128(x)[0])
+
+
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e4m3")])
 def test_block_dot_fmt_is_exact_sum_rounded_once(orc, fa, fb):
     """The block sum with E5M2 operands needs up to ~70 bits: it must equal the exact
