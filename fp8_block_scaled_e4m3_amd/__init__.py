@@ -71,6 +71,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_quantize_fp8_1x128.argtypes = [P, I, L, I, I, P, L, P, L, P]
     lib.dg_quantize_fp8_1x128.restype = I
     lib.dg_quantize_fp8_128x128.argtypes = [P, I, L, I, I, P, L, P, P]
+    lib.dg_quantize_fp8_1x128_fmt.argtypes = [P, I, L, I, I, P, L, P, L, I, P]
+    lib.dg_quantize_fp8_1x128_fmt.restype = I
+    lib.dg_quantize_fp8_128x128_fmt.argtypes = [P, I, L, I, I, P, L, P, I, P]
+    lib.dg_quantize_fp8_128x128_fmt.restype = I
     lib.dg_quantize_fp8_128x128.restype = I
     lib.dg_set_kernel_config.argtypes = [I]
     lib.dg_set_kernel_config.restype = I
@@ -268,32 +272,46 @@ def _quant_args(x, q, name):
     else:
         raise TypeError(f"{name}: x must be float32 or bfloat16, got {x.dtype}")
     px = _dev(x, "x", (torch.float32, torch.bfloat16), 2)
-    pq = _dev(q, "q", _fp8_types(), 2)
+    pq = _dev(q, "q", _fp8_any_types(), 2)
     if tuple(q.shape) != tuple(x.shape):
         raise ValueError(f"{name}: q shape {tuple(q.shape)} != x shape {tuple(x.shape)}")
     return dt, px, pq
 
 
 def dg_quantize_fp8_1x128(x, q, sa, stream=None) -> None:
-    """Cast x [rows, k] (fp32/bf16) to E4M3 q with per-1x128 scales sa [k/128, ld_sa] (MN-major)."""
+    """Cast x [rows, k] (fp32/bf16) to E4M3 q with per-1x128 scales sa [k/128, ld_sa]
+    (MN-major); a float8_e5m2 q receives E5M2 codes (see the _fmt call)."""
+    dg_quantize_fp8_1x128_fmt(x, q, sa, None, stream)
+
+
+def dg_quantize_fp8_1x128_fmt(x, q, sa, q_fmt=None, stream=None) -> None:
+    """The 1x128 cast with the output format "e4m3" or "e5m2" (scale amax/448 or amax/57344)."""
     rows, k = x.shape
-    dt, px, pq = _quant_args(x, q, "dg_quantize_fp8_1x128")
+    dt, px, pq = _quant_args(x, q, "dg_quantize_fp8_1x128_fmt")
+    fq = _fmt_of(q, q_fmt)
     psa = _dev(sa, "sa", _f32(), 2)
     if sa.shape[0] != -(-k // 128) or sa.shape[1] < rows:
         raise ValueError(f"sa shape {tuple(sa.shape)} does not fit rows={rows}, k={k}")
-    _check(load_library().dg_quantize_fp8_1x128(px, dt, x.stride(0), rows, k, pq, q.stride(0), psa, sa.stride(0),
-                                                _stream(stream)), "dg_quantize_fp8_1x128")
+    _check(load_library().dg_quantize_fp8_1x128_fmt(px, dt, x.stride(0), rows, k, pq, q.stride(0), psa,
+                                                    sa.stride(0), fq, _stream(stream)), "dg_quantize_fp8_1x128_fmt")
 
 
 def dg_quantize_fp8_128x128(x, q, sb, stream=None) -> None:
-    """Cast x [rows, k] (fp32/bf16) to E4M3 q with per-128x128 scales sb [ceil(rows/128), k/128]."""
+    """Cast x [rows, k] (fp32/bf16) to E4M3 q with per-128x128 scales sb [ceil(rows/128), k/128];
+    a float8_e5m2 q receives E5M2 codes (see the _fmt call)."""
+    dg_quantize_fp8_128x128_fmt(x, q, sb, None, stream)
+
+
+def dg_quantize_fp8_128x128_fmt(x, q, sb, q_fmt=None, stream=None) -> None:
+    """The 128x128 cast with the output format "e4m3" or "e5m2"."""
     rows, k = x.shape
-    dt, px, pq = _quant_args(x, q, "dg_quantize_fp8_128x128")
+    dt, px, pq = _quant_args(x, q, "dg_quantize_fp8_128x128_fmt")
+    fq = _fmt_of(q, q_fmt)
     psb = _dev(sb, "sb", _f32(), 2)
     if tuple(sb.shape) != (-(-rows // 128), -(-k // 128)) or not sb.is_contiguous():
         raise ValueError(f"sb must be contiguous [{-(-rows // 128)}, {-(-k // 128)}], got {tuple(sb.shape)}")
-    _check(load_library().dg_quantize_fp8_128x128(px, dt, x.stride(0), rows, k, pq, q.stride(0), psb,
-                                                  _stream(stream)), "dg_quantize_fp8_128x128")
+    _check(load_library().dg_quantize_fp8_128x128_fmt(px, dt, x.stride(0), rows, k, pq, q.stride(0), psb, fq,
+                                                      _stream(stream)), "dg_quantize_fp8_128x128_fmt")
 
 
 def dg_set_kernel_config(config_id: int) -> None:
@@ -338,5 +356,5 @@ __all__ = [
     "dg_get_m_alignment", "dg_set_num_cus", "dg_get_num_cus",
     "dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "DG_FMT_E4M3", "DG_FMT_E5M2", "dg_m_grouped_gemm_fp8_contiguous", "dg_m_grouped_gemm_fp8_masked",
     "dg_m_grouped_gemm_fp8_contiguous_fmt", "dg_m_grouped_gemm_fp8_masked_fmt",
-    "dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_set_kernel_config", "dg_kernel_config_info", "dg_plan_tiles", "dg_describe_launch",
+    "dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_fmt", "dg_quantize_fp8_128x128_fmt", "dg_set_kernel_config", "dg_kernel_config_info", "dg_plan_tiles", "dg_describe_launch",
 ]

@@ -302,13 +302,32 @@ static int check_quant(const void* x, int x_dtype, long ldx, int rows, int k, co
     return DG_OK;
 }
 
-int dg_quantize_fp8_1x128(const void* x, int x_dtype, long ldx, int rows, int k, void* q, long ldq, float* sa,
-                          long ld_sa, void* stream) {
+int dg_quantize_fp8_1x128_fmt(const void* x, int x_dtype, long ldx, int rows, int k, void* q, long ldq, float* sa,
+                              long ld_sa, int q_fmt, void* stream) {
+    if (!valid_fmt(q_fmt)) return DG_ERR_INVALID_ARG;
     const int st = check_quant(x, x_dtype, ldx, rows, k, q, ldq, sa);
     if (st != DG_OK || rows == 0) return st;
     if (ld_sa < rows) return DG_ERR_INVALID_ARG;
     if (dg::launch_quant_1x128(x, x_dtype == DG_DTYPE_BF16, ldx, rows, k, static_cast<uint8_t*>(q), ldq, sa, ld_sa,
-                               static_cast<hipStream_t>(stream)) != hipSuccess) {
+                               q_fmt == DG_FMT_E5M2, static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
+    }
+    return DG_OK;
+}
+
+int dg_quantize_fp8_1x128(const void* x, int x_dtype, long ldx, int rows, int k, void* q, long ldq, float* sa,
+                          long ld_sa, void* stream) {
+    return dg_quantize_fp8_1x128_fmt(x, x_dtype, ldx, rows, k, q, ldq, sa, ld_sa, DG_FMT_E4M3, stream);
+}
+
+int dg_quantize_fp8_128x128_fmt(const void* x, int x_dtype, long ldx, int rows, int k, void* q, long ldq, float* sb,
+                                int q_fmt, void* stream) {
+    if (!valid_fmt(q_fmt)) return DG_ERR_INVALID_ARG;
+    const int st = check_quant(x, x_dtype, ldx, rows, k, q, ldq, sb);
+    if (st != DG_OK || rows == 0) return st;
+    if (dg::launch_quant_128x128(x, x_dtype == DG_DTYPE_BF16, ldx, rows, k, static_cast<uint8_t*>(q), ldq, sb,
+                                 q_fmt == DG_FMT_E5M2, static_cast<hipStream_t>(stream)) != hipSuccess) {
         (void)hipGetLastError();
         return DG_ERR_HIP;
     }
@@ -317,14 +336,7 @@ int dg_quantize_fp8_1x128(const void* x, int x_dtype, long ldx, int rows, int k,
 
 int dg_quantize_fp8_128x128(const void* x, int x_dtype, long ldx, int rows, int k, void* q, long ldq, float* sb,
                             void* stream) {
-    const int st = check_quant(x, x_dtype, ldx, rows, k, q, ldq, sb);
-    if (st != DG_OK || rows == 0) return st;
-    if (dg::launch_quant_128x128(x, x_dtype == DG_DTYPE_BF16, ldx, rows, k, static_cast<uint8_t*>(q), ldq, sb,
-                                 static_cast<hipStream_t>(stream)) != hipSuccess) {
-        (void)hipGetLastError();
-        return DG_ERR_HIP;
-    }
-    return DG_OK;
+    return dg_quantize_fp8_128x128_fmt(x, x_dtype, ldx, rows, k, q, ldq, sb, DG_FMT_E4M3, stream);
 }
 
 int dg_kernel_config_info(int index, int* out) {

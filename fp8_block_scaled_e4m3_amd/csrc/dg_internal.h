@@ -42,9 +42,10 @@ struct KernelConfig {
 const KernelConfig* kernel_configs(int* count);
 
 // FP8 casts with fine-grained scales (defined in dg_quant.hip).
+// q_e5m2: codes in E5M2 (scale amax / 57344) instead of E4M3 (amax / 448)
 hipError_t launch_quant_1x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq, float* sa,
-                              long ld_sa, hipStream_t stream);
+                              long ld_sa, int q_e5m2, hipStream_t stream);
 hipError_t launch_quant_128x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq,
-                                float* sb, hipStream_t stream);
+                                float* sb, int q_e5m2, hipStream_t stream);
 
 }  // namespace dg

@@ -1,5 +1,5 @@
-// dg_quant.hip -- gfx950 kernels that cast fp32 / bf16 matrices to E4M3 with the
-// fine-grained scales the GEMM consumes.
+// dg_quant.hip -- gfx950 kernels that cast fp32 / bf16 matrices to E4M3 (or E5M2)
+// with the fine-grained scales the GEMM consumes.
 //
 // The README ("DeepGEMM: clean and efficient FP8 GEMM kernels", nipponese.news
 // translation, usage paragraph) leaves the FP8 cast and the transposition of the
@@ -10,6 +10,8 @@
 // Per block: amax = max |x| (NaN entries do not raise it), scale = fp32(amax / 448)
 // (1 when amax is 0), q = E4M3 round-to-nearest-even of fp32(x / scale), saturating
 // at +-448 (the format's largest finite value), NaN -> 0x7F, sign of zero kept.
+// E5M2 output (the blog's other FP8 format, hnwysp.cn section 2.3) is the same with
+// 57344, E5M2's largest finite value, in place of 448.
 // Both divisions are IEEE-correctly-rounded fp32 divisions, so the codes are a
 // deterministic function of the input.  Each kernel reads its input once.
 #include <hip/hip_runtime.h>
@@ -23,6 +25,7 @@ namespace {
 
 constexpr int kQBlock = 128;
 constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
 
 __device__ __forceinline__ float load_elem(const float* p) { return *p; }
 __device__ __forceinline__ float load_elem(const uint16_t* p) {
@@ -45,6 +48,43 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
     const uint32_t rounded = ab + 0x7FFFFu + ((ab >> 20) & 1u);
     return sign | ((rounded >> 20) - (120u << 3));     // rebias exponent 127 -> 7
 }
+
+// E5M2 code of an fp32 value, round to nearest even, saturating (bias 15, two
+// stored mantissa bits, subnormals are the multiples of 2^-16 below 2^-14).
+__device__ __forceinline__ uint32_t e5m2_code(float y) {
+    const uint32_t bits = __float_as_uint(y);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (!(a == a)) return 0x7Fu;                       // NaN
+    if (a >= kE5M2Max) return sign | 0x7Bu;            // saturate at 57344
+    if (a < 0x1p-14f) {                                // below 2^-14: multiples of 2^-16
+        const float q = __builtin_rintf(a * 65536.0f); // exact scaling, RNE (q <= 4)
+        return sign | (uint32_t)q;                     // q == 4 is the smallest normal
+    }
+    // normal range: keep 2 of 23 mantissa bits, ties to even, carry into the exponent
+    const uint32_t ab = bits & 0x7FFFFFFFu;
+    const uint32_t rounded = ab + 0xFFFFFu + ((ab >> 21) & 1u);
+    return sign | ((rounded >> 21) - (112u << 2));     // rebias exponent 127 -> 15
+}
+
+// Output format FMT: 0 = E4M3, 1 = E5M2.
+template <int FMT> struct Fp8Out;
+template <> struct Fp8Out<0> {
+    static constexpr float kMax = kE4M3Max;
+    static __device__ __forceinline__ uint32_t code(float y) { return e4m3_code(y); }
+    template <bool HI>
+    static __device__ __forceinline__ int pack(float a, float b, int old) {
+        return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+    }
+};
+template <> struct Fp8Out<1> {
+    static constexpr float kMax = kE5M2Max;
+    static __device__ __forceinline__ uint32_t code(float y) { return e5m2_code(y); }
+    template <bool HI>
+    static __device__ __forceinline__ int pack(float a, float b, int old) {
+        return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+    }
+};
 
 // One 16-byte load: 4 fp32 or 8 bf16 values, widened to fp32 (bf16 -> fp32 is exact).
 template <typename T> struct Vec;
@@ -94,20 +134,20 @@ __device__ __forceinline__ float div_fast(float x, float scale, float r) {
 
 // N codes of v / scale packed little-endian (4 -> one dword, 8 -> two).  Fast path
 // (every value of the wave finite or infinite but not NaN, the scale in range): the
-// quotient as above and gfx950's E4M3 convert, which rounds to nearest even with
-// subnormals and, for the magnitudes here (|q| <= 448 up to one rounding), agrees
-// with e4m3_code.  Otherwise each code is computed in software with an IEEE division.
-template <int N>
+// quotient as above and gfx950's FP8 convert (E4M3 or E5M2), which rounds to nearest
+// even with subnormals and, for the magnitudes here (|q| at most the format's
+// largest value up to one rounding), agrees with the software encoder.  Otherwise
+// each code is computed in software with an IEEE division.
+template <int N, int FMT>
 __device__ __forceinline__ void store_codes(uint8_t* dst, const float* v, float scale, bool fast) {
+    using F = Fp8Out<FMT>;
     uint32_t w[N / 4];
     if (fast) {
         const float r = 1.0f / scale;
 #pragma unroll
         for (int d = 0; d < N / 4; ++d) {
-            int c = __builtin_amdgcn_cvt_pk_fp8_f32(div_fast(v[4 * d], scale, r), div_fast(v[4 * d + 1], scale, r), 0,
-                                                    false);
-            c = __builtin_amdgcn_cvt_pk_fp8_f32(div_fast(v[4 * d + 2], scale, r), div_fast(v[4 * d + 3], scale, r), c,
-                                                true);
+            int c = F::template pack<false>(div_fast(v[4 * d], scale, r), div_fast(v[4 * d + 1], scale, r), 0);
+            c = F::template pack<true>(div_fast(v[4 * d + 2], scale, r), div_fast(v[4 * d + 3], scale, r), c);
             w[d] = (uint32_t)c;
         }
     } else {
@@ -115,7 +155,7 @@ __device__ __forceinline__ void store_codes(uint8_t* dst, const float* v, float 
         for (int d = 0; d < N / 4; ++d) {
             uint32_t c = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) c |= e4m3_code(v[4 * d + e] / scale) << (8 * e);
+            for (int e = 0; e < 4; ++e) c |= F::code(v[4 * d + e] / scale) << (8 * e);
             w[d] = c;
         }
     }
@@ -140,7 +180,7 @@ __device__ __forceinline__ bool wave_all(bool b) { return __ballot(!b) == 0; }
 // workgroup reads long contiguous stretches of each row.
 constexpr int kRowsPerThread = 4;
 
-template <typename T>
+template <typename T, int FMT>
 __global__ void __launch_bounds__(256)
 quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, uint8_t* __restrict__ q, long ldq,
                    float* __restrict__ sa, long ld_sa) {
@@ -169,10 +209,10 @@ quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, uin
             const float o = __shfl_xor(amax, off, L);
             amax = o > amax ? o : amax;
         }
-        const float scale = amax == 0.f ? 1.f : amax / kE4M3Max;
+        const float scale = amax == 0.f ? 1.f : amax / Fp8Out<FMT>::kMax;
         const unsigned row = g / (unsigned)kblocks, kb = g - row * (unsigned)kblocks;
         const bool fast = wave_all(fast_scale(scale) && !any_nan(v[r], N));
-        store_codes<N>(q + (long)row * ldq + kb * kQBlock + lg * N, v[r], scale, fast);
+        store_codes<N, FMT>(q + (long)row * ldq + kb * kQBlock + lg * N, v[r], scale, fast);
         if (lg == 0) sa[(long)kb * ld_sa + row] = scale;
     }
 }
@@ -181,7 +221,7 @@ quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, uin
 // whole 512-byte (fp32) or 256-byte (bf16) row segments: lane t of a pass covers
 // row pass*RPP + t/L, columns (t%L)*N .. +N.  All passes' loads are in flight
 // before the reduction.
-template <typename T>
+template <typename T, int FMT>
 __global__ void __launch_bounds__(256)
 quant_128x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, uint8_t* __restrict__ q, long ldq,
                      float* __restrict__ sb) {
@@ -213,7 +253,7 @@ quant_128x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, u
     amax = s_amax[0];
 #pragma unroll
     for (int w = 1; w < 4; ++w) amax = s_amax[w] > amax ? s_amax[w] : amax;
-    const float scale = amax == 0.f ? 1.f : amax / kE4M3Max;
+    const float scale = amax == 0.f ? 1.f : amax / Fp8Out<FMT>::kMax;
     if (t == 0) sb[(long)rb * kblocks + kb] = scale;
     bool nan = false;
 #pragma unroll
@@ -222,14 +262,17 @@ quant_128x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, u
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
         const int row = r0 + i * RPP;
-        if (row < rows) store_codes<N>(q + (long)row * ldq + c0, v[i], scale, fast);
+        if (row < rows) store_codes<N, FMT>(q + (long)row * ldq + c0, v[i], scale, fast);
     }
 }
 
 }  // namespace
 
-hipError_t launch_quant_1x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq, float* sa,
-                              long ld_sa, hipStream_t stream) {
+namespace {
+
+template <int FMT>
+hipError_t launch_1x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq, float* sa,
+                        long ld_sa, hipStream_t stream) {
     const int kblocks = k / kQBlock;
     const long per_wg = (x_bf16 ? 256 / 16 : 256 / 32) * (long)kRowsPerThread;   // groups per workgroup
     // row chunks small enough for 32-bit group indices inside the kernel
@@ -238,11 +281,11 @@ hipError_t launch_quant_1x128(const void* x, int x_bf16, long ldx, int rows, int
         const int nr = (int)(rows - r0 < chunk ? rows - r0 : chunk);
         const long blocks = ((long)nr * kblocks + per_wg - 1) / per_wg;
         if (x_bf16)
-            hipLaunchKernelGGL(quant_1x128_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+            hipLaunchKernelGGL((quant_1x128_kernel<uint16_t, FMT>), dim3((unsigned)blocks), dim3(256), 0, stream,
                                static_cast<const uint16_t*>(x) + r0 * ldx, ldx, nr, kblocks, q + r0 * ldq, ldq,
                                sa + r0, ld_sa);
         else
-            hipLaunchKernelGGL(quant_1x128_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+            hipLaunchKernelGGL((quant_1x128_kernel<float, FMT>), dim3((unsigned)blocks), dim3(256), 0, stream,
                                static_cast<const float*>(x) + r0 * ldx, ldx, nr, kblocks, q + r0 * ldq, ldq, sa + r0,
                                ld_sa);
         const hipError_t e = hipGetLastError();
@@ -251,17 +294,32 @@ hipError_t launch_quant_1x128(const void* x, int x_bf16, long ldx, int rows, int
     return hipSuccess;
 }
 
-hipError_t launch_quant_128x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq,
-                                float* sb, hipStream_t stream) {
+template <int FMT>
+hipError_t launch_128x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq, float* sb,
+                          hipStream_t stream) {
     const int kblocks = k / kQBlock;
     const dim3 grid((unsigned)kblocks, (unsigned)((rows + kQBlock - 1) / kQBlock));
     if (x_bf16)
-        hipLaunchKernelGGL(quant_128x128_kernel<uint16_t>, grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((quant_128x128_kernel<uint16_t, FMT>), grid, dim3(256), 0, stream,
                            static_cast<const uint16_t*>(x), ldx, rows, kblocks, q, ldq, sb);
     else
-        hipLaunchKernelGGL(quant_128x128_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(x),
-                           ldx, rows, kblocks, q, ldq, sb);
+        hipLaunchKernelGGL((quant_128x128_kernel<float, FMT>), grid, dim3(256), 0, stream,
+                           static_cast<const float*>(x), ldx, rows, kblocks, q, ldq, sb);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_1x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq, float* sa,
+                              long ld_sa, int q_e5m2, hipStream_t stream) {
+    return q_e5m2 ? launch_1x128<1>(x, x_bf16, ldx, rows, k, q, ldq, sa, ld_sa, stream)
+                  : launch_1x128<0>(x, x_bf16, ldx, rows, k, q, ldq, sa, ld_sa, stream);
+}
+
+hipError_t launch_quant_128x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq,
+                                float* sb, int q_e5m2, hipStream_t stream) {
+    return q_e5m2 ? launch_128x128<1>(x, x_bf16, ldx, rows, k, q, ldq, sb, stream)
+                  : launch_128x128<0>(x, x_bf16, ldx, rows, k, q, ldq, sb, stream);
 }
 
 }  // namespace dg

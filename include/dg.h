@@ -172,6 +172,17 @@ int dg_quantize_fp8_1x128(const void* x, int x_dtype, long ldx, int rows, int k,
 int dg_quantize_fp8_128x128(const void* x, int x_dtype, long ldx, int rows, int k,
                             void* q, long ldq, float* sb, void* stream);
 
+/* The two casts with the output format chosen: q_fmt DG_FMT_E4M3 (exactly the
+ * calls above) or DG_FMT_E5M2, E5M2 being the blog's other FP8 format (hnwysp.cn
+ * DeepGEMM blog, section 2.3).  For E5M2 the scale is fp32(amax / 57344), the
+ * codes are E5M2 RNE of fp32(x / scale) saturating at +-57344 (E5M2's largest
+ * finite value; never an infinity), NaN -> 0x7F; everything else as above.  An
+ * unknown q_fmt is DG_ERR_INVALID_ARG. */
+int dg_quantize_fp8_1x128_fmt(const void* x, int x_dtype, long ldx, int rows, int k,
+                              void* q, long ldq, float* sa, long ld_sa, int q_fmt, void* stream);
+int dg_quantize_fp8_128x128_fmt(const void* x, int x_dtype, long ldx, int rows, int k,
+                                void* q, long ldq, float* sb, int q_fmt, void* stream);
+
 /* Pin the kernel configuration (an id reported by dg_describe_launch) for every
  * later call of that configuration's layout, overriding the planner; -1 restores
  * automatic planning for all layouts.  Meant for tuning and for tests that

@@ -202,3 +202,10 @@ def test_quantize_validation(lib):
     assert q2(P(16), 1, 256, 4, 384, P(16), 384, P(16), None) == dg.DG_ERR_INVALID_ARG       # ldx < k
     assert q2(P(16), 1, 388, 4, 384, P(16), 384, P(16), None) == dg.DG_ERR_MISALIGNED        # ldx*2 % 16
     assert q2(P(16), 1, 384, 0, 384, P(16), 384, P(16), None) == dg.DG_OK
+    # output format: unknown codes rejected first; the E5M2 forms validate like the plain ones
+    q1f, q2f = lib.dg_quantize_fp8_1x128_fmt, lib.dg_quantize_fp8_128x128_fmt
+    assert q1f(P(16), 0, 256, 4, 256, P(16), 256, P(16), 4, 2, None) == dg.DG_ERR_INVALID_ARG
+    assert q2f(P(16), 0, 256, 4, 256, P(16), 256, P(16), -1, None) == dg.DG_ERR_INVALID_ARG
+    assert q1f(P(16), 0, 256, 4, 200, P(16), 256, P(16), 4, 1, None) == dg.DG_ERR_UNSUPPORTED
+    assert q2f(P(16), 1, 388, 4, 384, P(16), 384, P(16), 1, None) == dg.DG_ERR_MISALIGNED
+    assert q1f(P(16), 0, 256, 0, 256, P(16), 256, P(16), 4, 1, None) == dg.DG_OK

@@ -1,5 +1,6 @@
 """GPU parity of the FP8 cast kernels (the prior-kernel cast the README leaves to the
-caller) against the oracle's quantiser: codes and scales must match bit for bit."""
+caller) against the oracle's quantiser: codes and scales must match bit for bit, for
+E4M3 output and for E5M2 output (the blog's other FP8 format)."""
 import numpy as np
 import pytest
 
@@ -46,20 +47,26 @@ def as_bf16(x):
     return t, t.to(torch.float32).numpy()
 
 
-def gpu_1x128(x_t, rows, k):
+def gpu_1x128(x_t, rows, k, fmt="e4m3"):
     import torch
     q = torch.empty((rows, k), dtype=torch.uint8, device="cuda:0")
     sa = torch.full((k // 128, W.ld_sa_for(rows)), -1.0, device="cuda:0")
-    dg.dg_quantize_fp8_1x128(x_t, q, sa)
+    if fmt == "e4m3":
+        dg.dg_quantize_fp8_1x128(x_t, q, sa)
+    else:
+        dg.dg_quantize_fp8_1x128_fmt(x_t, q, sa, q_fmt=fmt)
     torch.cuda.synchronize()
     return q.cpu().numpy(), sa.cpu().numpy()
 
 
-def gpu_128x128(x_t, rows, k):
+def gpu_128x128(x_t, rows, k, fmt="e4m3"):
     import torch
     q = torch.empty((rows, k), dtype=torch.uint8, device="cuda:0")
     sb = torch.full((-(-rows // 128), k // 128), -1.0, device="cuda:0")
-    dg.dg_quantize_fp8_128x128(x_t, q, sb)
+    if fmt == "e4m3":
+        dg.dg_quantize_fp8_128x128(x_t, q, sb)
+    else:
+        dg.dg_quantize_fp8_128x128_fmt(x_t, q, sb, q_fmt=fmt)
     torch.cuda.synchronize()
     return q.cpu().numpy(), sb.cpu().numpy()
 
@@ -70,7 +77,8 @@ def same_bits(a, b):
 
 @pytest.mark.parametrize("rows,k", [(1, 128), (7, 384), (300, 640), (129, 1024)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_quant_1x128_bit_exact(orc, rows, k, dtype):
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quant_1x128_bit_exact(orc, rows, k, dtype, fmt):
     import torch
     x = recipe(rows, k, 1, seed=rows * 7 + k)
     if rows >= 8:
@@ -80,9 +88,9 @@ def test_quant_1x128_bit_exact(orc, rows, k, dtype):
         xt = xt.to("cuda:0")
     else:
         xt = to_dev(x)
-    say(f"quant 1x128 {rows}x{k} {dtype}")
-    q, sa = gpu_1x128(xt, rows, k)
-    rq, rsa = orc.quantize_rows_1x128(x)
+    say(f"quant 1x128 {rows}x{k} {dtype} {fmt}")
+    q, sa = gpu_1x128(xt, rows, k, fmt)
+    rq, rsa = orc.quantize_rows_1x128(x, fmt)
     assert np.array_equal(q, rq), f"{np.sum(q != rq)} codes differ"
     assert same_bits(sa[:, :rows], rsa)
     assert np.all(sa[:, rows:] == -1.0)                     # padding columns untouched
@@ -121,9 +129,43 @@ def test_quant_conversion_grid_bit_exact(orc):
     assert np.array_equal(q, rq), f"{np.sum(q != rq)} codes differ"
 
 
+def e5m2_rounding_grid():
+    """fp32 values at and around every E5M2 rounding decision in [-57344, 57344]: each
+    representable value, each tie between neighbours and the fp32 values one ulp to
+    either side of it, for normal and subnormal codes, plus values that round to 0."""
+    vals = []
+    for e in range(-17, 16):                     # E5M2 exponents (normal from -14, spacing 2^(e-2))
+        for m in range(8):
+            for frac in (0.0, 0.5):
+                v = np.float32(2.0 ** e * (1 + (m + frac) / 4)) if e >= -14 else np.float32((m + frac) * 2.0 ** -16)
+                vals += [v, np.nextafter(v, np.float32(0)), np.nextafter(v, np.float32(1e9))]
+    vals += [np.float32(2.0 ** -17), np.float32(2.0 ** -18), np.float32(1e-30), np.float32(0.0)]
+    v = np.array(vals, np.float32)
+    v = v[np.abs(v) <= 57344]
+    return np.concatenate([v, -v])
+
+
+def test_quant_e5m2_conversion_grid_bit_exact(orc):
+    """With 57344 in every block the E5M2 scale is exactly 1, so the codes are the E5M2
+    conversion itself: every rounding decision of the format, both signs, compared
+    with the oracle's encoder."""
+    grid = e5m2_rounding_grid()
+    per = 127
+    nblk = -(-grid.size // per)
+    nblk += -nblk % 4                             # four blocks per row
+    body = np.resize(grid, nblk * per).reshape(nblk, per)
+    x = np.concatenate([np.full((nblk, 1), 57344.0, np.float32), body], axis=1).reshape(-1, 128 * 4)
+    rows = x.shape[0]
+    q, sa = gpu_1x128(to_dev(x), rows, x.shape[1], "e5m2")
+    rq, rsa = orc.quantize_rows_1x128(x, "e5m2")
+    assert np.all(sa[:, :rows] == 1.0)
+    assert np.array_equal(q, rq), f"{np.sum(q != rq)} codes differ"
+
+
 @pytest.mark.parametrize("rows,k", [(128, 128), (200, 384), (1, 256), (385, 512)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_quant_128x128_bit_exact(orc, rows, k, dtype):
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quant_128x128_bit_exact(orc, rows, k, dtype, fmt):
     x = recipe(rows, k, 128, seed=rows * 11 + k)
     if rows >= 8:
         x = specials(x)
@@ -132,9 +174,9 @@ def test_quant_128x128_bit_exact(orc, rows, k, dtype):
         xt = xt.to("cuda:0")
     else:
         xt = to_dev(x)
-    say(f"quant 128x128 {rows}x{k} {dtype}")
-    q, sb = gpu_128x128(xt, rows, k)
-    rq, rsb = orc.quantize_blocks_128x128(x)
+    say(f"quant 128x128 {rows}x{k} {dtype} {fmt}")
+    q, sb = gpu_128x128(xt, rows, k, fmt)
+    rq, rsb = orc.quantize_blocks_128x128(x, fmt)
     assert np.array_equal(q, rq), f"{np.sum(q != rq)} codes differ"
     assert same_bits(sb, rsb)
 
@@ -179,6 +221,29 @@ def test_cast_then_gemm_end_to_end(orc):
     check_values(bits(d), orc.gemm_fp8_nt(ra, rsa, rb, rsb), "cast + gemm")
 
 
+def test_e5m2_cast_then_gemm_end_to_end(orc):
+    """E5M2 casts on the GPU (selected by float8_e5m2 output tensors) followed by the GPU
+    GEMM with E5M2 operands match the oracle GEMM of the oracle's E5M2 casts."""
+    import torch
+    m, n, k = 192, 208, 512
+    rng = np.random.default_rng(6)
+    xa, xb = W._scaled_normals(rng, m, k, 1), W._scaled_normals(rng, n, k, 128)
+    qa = torch.empty((m, k), dtype=torch.float8_e5m2, device="cuda:0")
+    sa = torch.empty((k // 128, W.ld_sa_for(m)), device="cuda:0")
+    qb = torch.empty((n, k), dtype=torch.float8_e5m2, device="cuda:0")
+    sb = torch.empty((-(-n // 128), k // 128), device="cuda:0")
+    d = sentinel_like((m, n))
+    dg.dg_quantize_fp8_1x128(to_dev(xa), qa, sa)
+    dg.dg_quantize_fp8_128x128(to_dev(xb), qb, sb)
+    dg.dg_gemm_fp8_nt(qa, sa, qb, sb, d)
+    torch.cuda.synchronize()
+    ra, rsa = orc.quantize_rows_1x128(xa, "e5m2")
+    rb, rsb = orc.quantize_blocks_128x128(xb, "e5m2")
+    assert np.array_equal(qa.view(torch.uint8).cpu().numpy(), ra)
+    assert np.array_equal(qb.view(torch.uint8).cpu().numpy(), rb)
+    check_values(bits(d), orc.gemm_fp8_nt(ra, rsa, rb, rsb, a_fmt="e5m2", b_fmt="e5m2"), "e5m2 cast + gemm")
+
+
 def test_quant_validation_errors():
     import torch
     x = torch.zeros((4, 200), device="cuda:0")
@@ -187,3 +252,7 @@ def test_quant_validation_errors():
     with pytest.raises(dg.DGError) as e:
         dg.dg_quantize_fp8_1x128(x, q, sa)
     assert e.value.status == dg.DG_ERR_UNSUPPORTED
+    x = torch.zeros((4, 256), device="cuda:0")
+    q = torch.zeros((4, 256), dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(ValueError):
+        dg.dg_quantize_fp8_1x128_fmt(x, q, sa, q_fmt="e3m4")
