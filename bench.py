@@ -32,10 +32,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the library sources with comments and blank space removed, so that the
+    stored traffic counters stay valid across comment edits and lapse on code edits."""
+    import re
     h = hashlib.sha256()
     for name in ("dg_gemm.hip", "dg_quant.hip", "dg_internal.h", "dg_api.cpp"):
-        with open(os.path.join(ROOT, "fp8_block_scaled_e4m3_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "fp8_block_scaled_e4m3_amd", "csrc", name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

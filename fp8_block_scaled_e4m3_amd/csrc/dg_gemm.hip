@@ -7,7 +7,8 @@
 //   D[m,n] = bf16( sum_kb sA[m,kb] * sB[n/128,kb] * sum_{k in kb} A[m,k] * B[n,k] )
 //
 // How it maps onto gfx950:
-//  * One V_MFMA_F32_16X16X128_F8F6F4 (E4M3 x E4M3) covers exactly one 128-wide
+//  * One V_MFMA_F32_16X16X128_F8F6F4 (E4M3 x E4M3; either operand E5M2 through
+//    the instruction's format fields, FMT below) covers exactly one 128-wide
 //    K block of a 16x16 output sub-tile, so each K block's partial is produced
 //    by a single MFMA with a zero accumulator and is promoted at once:
 //    acc = fma(partial, sA*sB, acc) in fp32, K blocks ascending (the README's
@@ -120,7 +121,9 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                const uint8_t* __restrict__ b_ptr, const float* __restrict__ sb_ptr, uint16_t* __restrict__ d_ptr) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FMT_SRC0 = (FMT >> 1) & 1, FMT_SRC1 = FMT & 1;   // 0 = FP8 E4M3, 1 = BF8 E5M2
+    // operand formats (FMT bit 0: A is E5M2, bit 1: B is E5M2); the MFMA's first
+    // source carries B rows and its second A rows.  Field values: 0 = E4M3, 1 = E5M2
+    constexpr int FMT_SRC0 = (FMT >> 1) & 1, FMT_SRC1 = FMT & 1;
     constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int NACC = MF * MF / 64;             // accumulator floats per lane per sub-tile
     constexpr int ROWS = BM + BN;
