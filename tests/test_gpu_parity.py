@@ -328,6 +328,71 @@ def test_masked_graph_replay_reads_device_counts(orc):
         check_masked(orc, dict(md, masked_m=np.array(counts, np.int32)), got)
 
 
+def test_dense_and_contiguous_graph_replays_match_eager(orc):
+    """Dense and contiguous calls captured into one graph give, on every replay (with
+    eager work and synchronisation between replays and the inputs changed on the
+    device in between), the eager calls' output bit for bit."""
+    import torch
+    dd = W.make_dense(320, 464, 512, seed=41)
+    cd = W.make_contiguous([200, 5, 130], n=208, k=384, seed=42)
+    dv, cv = upload(dd), upload(cd)
+    od, oc = sentinel_like((320, 464)), sentinel_like((cd["m_total"], 208))
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):      # warm-up outside capture
+        dg.dg_gemm_fp8_nt(dv["a"], dv["sa"], dv["b"], dv["sb"], od)
+        dg.dg_m_grouped_gemm_fp8_contiguous(cv["a"], cv["sa"], cv["b"], cv["sb"], oc, cv["m_indices"])
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dg.dg_gemm_fp8_nt(dv["a"], dv["sa"], dv["b"], dv["sb"], od)
+        dg.dg_m_grouped_gemm_fp8_contiguous(cv["a"], cv["sa"], cv["b"], cv["sb"], oc, cv["m_indices"])
+    valid = cd["m_indices"] >= 0
+    for rep in range(3):
+        say(f"graph replay dense + contiguous, replay {rep}")
+        if rep == 2:                      # new operands, written on the device
+            dd = W.make_dense(320, 464, 512, seed=43)
+            for key in ("a", "sa", "b", "sb"):
+                dv[key].copy_(torch.from_numpy(dd[key]))
+        od.fill_(W.SENTINEL_BF16)
+        oc.fill_(W.SENTINEL_BF16)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_d, got_c = bits(od), bits(oc)
+        eager_d, _ = run_dense(dd, pad_cols=0)
+        eager_c = run_contiguous(cd)
+        assert np.array_equal(got_d, eager_d), f"dense replay {rep} differs from the eager call"
+        assert np.array_equal(got_c, eager_c), f"contiguous replay {rep} differs from the eager call"
+        assert np.all(got_c[~valid] == W.SENTINEL_BF16)
+    check_values(got_d, oracle_dense(orc, dd), "dense after graph replays")
+
+
+def test_concurrent_streams_independent(orc):
+    """Calls on two streams run concurrently (each grid fills the GPU, so they interleave
+    on the hardware) and each result equals that call run alone."""
+    import torch
+    d1 = W.make_dense(1024, 2048, 1024, seed=44)
+    d2 = W.make_dense(512, 4096, 2048, seed=45)
+    alone1, _ = run_dense(d1, pad_cols=0)
+    alone2, _ = run_dense(d2, pad_cols=0)
+    v1, v2 = upload(d1), upload(d2)
+    o1, o2 = sentinel_like((1024, 2048)), sentinel_like((512, 4096))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            dg.dg_gemm_fp8_nt(v1["a"], v1["sa"], v1["b"], v1["sb"], o1, stream=s1)
+        with torch.cuda.stream(s2):
+            dg.dg_gemm_fp8_nt(v2["a"], v2["sa"], v2["b"], v2["sb"], o2, stream=s2)
+    torch.cuda.synchronize()
+    say("two streams: 1024x2048x1024 and 512x4096x2048")
+    assert np.array_equal(bits(o1), alone1)
+    assert np.array_equal(bits(o2), alone2)
+    check_values(alone1, oracle_dense(orc, d1), "stream 1 alone")
+
+
 # --------------------------------------------------------------------------- errors
 def test_binding_reports_validation_errors():
     import torch
