@@ -321,10 +321,12 @@ def dg_set_kernel_config(config_id: int) -> None:
 
 def dg_kernel_config_info() -> list:
     """All compiled kernel configurations as dicts (id, layout, block_m, block_n, waves,
-    all_formats: whether E5M2 operands run in it)."""
-    out, res, i = (ctypes.c_int * 6)(), [], 0
+    all_formats: whether E5M2 operands run in it, k_specialised: whether it has
+    instances compiled for fixed K)."""
+    out, res, i = (ctypes.c_int * 7)(), [], 0
     while load_library().dg_kernel_config_info(i, out) == DG_OK:
-        res.append(dict(zip(("id", "layout", "block_m", "block_n", "waves", "all_formats"), list(out))))
+        res.append(dict(zip(("id", "layout", "block_m", "block_n", "waves", "all_formats", "k_specialised"),
+                            list(out))))
         i += 1
     return res
 
@@ -344,10 +346,11 @@ def dg_plan_tiles(m: int, n: int, num_units: int, block_ms, block_ns, eff=None, 
 
 def dg_describe_launch(layout: int, m: int, n: int, k: int, num_groups: int = 1, num_cus: int = 0) -> dict:
     """The launch a call of these sizes would make (layout 0 dense, 1 contiguous, 2 masked)."""
-    out = (ctypes.c_int * 7)()
+    out = (ctypes.c_int * 8)()
     r = load_library().dg_describe_launch(layout, m, n, k, num_groups, num_cus, out)
     _check(r, "dg_describe_launch")
-    keys = ("block_m", "block_n", "waves_per_workgroup", "tiles", "grid", "config_id", "group_m")
+    keys = ("block_m", "block_n", "waves_per_workgroup", "tiles", "grid", "config_id", "group_m",
+            "k_blocks_specialised")
     return dict(zip(keys, list(out)))
 
 

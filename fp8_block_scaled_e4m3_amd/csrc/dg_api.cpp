@@ -101,6 +101,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_fmt(int f) { return f == DG_FMT_E4M3 || f == DG_FMT_E5M2; }
 
+// K/128 of the compile-time-K instance a launch of config c uses, 0 for the generic one
+// (the selection made by the config's launcher: E4M3 operands, K/128 in kSpecKBlocks)
+int specialised_kblocks(const KernelConfig& c, const GemmParams& p) {
+    if (!c.k_specialised || p.fmt != 0) return 0;
+    for (int kb : dg::kSpecKBlocks)
+        if (p.kblocks == kb) return kb;
+    return 0;
+}
+
 // The kernels address a tile's operands through 32-bit buffer offsets from the
 // tile's first row: up to 256 rows of A or B (row stride lda / ldb bytes) plus the
 // K offset, and the A scales of all K blocks (k/128 rows of ld_sa floats).  Sizes
@@ -218,6 +227,7 @@ int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_
         describe_out[4] = (int)grid;
         describe_out[5] = c.id;
         describe_out[6] = layout == dg::kMasked ? 0 : p.group_m;
+        describe_out[7] = specialised_kblocks(c, p);
         return DG_OK;
     }
     if (debug_enabled())
@@ -349,6 +359,7 @@ int dg_kernel_config_info(int index, int* out) {
     out[3] = cfgs[index].bn;
     out[4] = cfgs[index].wm * cfgs[index].wn;
     out[5] = cfgs[index].all_formats ? 1 : 0;
+    out[6] = cfgs[index].k_specialised ? 1 : 0;
     return DG_OK;
 }
 

@@ -115,7 +115,9 @@ __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC0
 // FMT: operand formats, bit 0 = A is E5M2, bit 1 = B is E5M2 (else E4M3).  The
 // matrix instruction's format fields take them directly (B rows feed the
 // instruction's first operand, A rows its second).
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT>
+// KC > 0: an instance for K/128 == KC only (loop trip counts and the split into
+// stage groups are then compile-time constants); 0: any K.
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int KC>
 __global__ void __launch_bounds__(WM * WN * 64)
 dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const float* __restrict__ sa_ptr,
                const uint8_t* __restrict__ b_ptr, const float* __restrict__ sb_ptr, uint16_t* __restrict__ d_ptr) {
@@ -159,7 +161,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     const int wm = wave % WM, wn = wave / WM;
     const int lsub = lane & (MF - 1);             // row of the sub-tile this lane feeds / owns
     const int lgrp = lane / MF;                   // K group of the lane inside an operand fragment
-    const int KB = p.kblocks;
+    const int KB = KC > 0 ? KC : p.kblocks;
 
     // ---- masked layout: valid row blocks per group, exclusive prefix in LDS ----
     int total_tiles = p.num_tiles;
@@ -870,20 +872,34 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     if constexpr (PIPE) wait_vmem_le<0>();
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int KC = 0>
 static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE, FMT>), dim3(grid), dim3(WM * WN * 64), 0,
-                       s, p, p.a, p.sa, p.b, p.sb, p.d);
+    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE, FMT, KC>), dim3(grid),
+                       dim3(WM * WN * 64), 0, s, p, p.a, p.sa, p.b, p.sb, p.d);
     return hipGetLastError();
+}
+
+// the E4M3 instance for K/128 == KC (pipelined when KC splits into stage groups)
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, int KC>
+static hipError_t launch_spec(const GemmParams& p, int grid, hipStream_t s) {
+    return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK && KC % NST == 0, 0, KC>(p, grid, s);
 }
 
 // The pipelined variant runs the next tile's first NST blocks as the tail of the
 // current one, which needs the K blocks to split into whole groups of NST.  It is
 // compiled only for the configurations whose registers it fits (PIPE_OK).
 // Configurations with ALL_FMT also have E5M2-operand instances (per-tile variant);
-// the planner gives the others E4M3 operands only.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool ALL_FMT>
+// the planner gives the others E4M3 operands only.  Configurations with KSPEC have
+// E4M3 instances for each K/128 in kSpecKBlocks, used when the call's K matches.
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool ALL_FMT, bool KSPEC>
 static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
+    static_assert(sizeof(kSpecKBlocks) / sizeof(kSpecKBlocks[0]) == 2, "one branch per specialised K");
+    if constexpr (KSPEC) {
+        if (p.fmt == 0 && p.kblocks == kSpecKBlocks[0])
+            return launch_spec<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, kSpecKBlocks[0]>(p, grid, s);
+        if (p.fmt == 0 && p.kblocks == kSpecKBlocks[1])
+            return launch_spec<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, kSpecKBlocks[1]>(p, grid, s);
+    }
     if constexpr (ALL_FMT) {
         switch (p.fmt) {
             case 1: return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, 1>(p, grid, s);
@@ -902,8 +918,8 @@ static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
 template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK>
 static hipError_t occupancy_cfg(int* blocks) {
     typedef void (*KernelFn)(const GemmParams, const uint8_t*, const float*, const uint8_t*, const float*, uint16_t*);
-    const KernelFn k0 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, false, 0>;
-    const KernelFn k1 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, 0>;
+    const KernelFn k0 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, false, 0, 0>;
+    const KernelFn k1 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, 0, 0>;
     int b0 = 0, b1 = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, reinterpret_cast<const void*>(k0), WM * WN * 64, 0);
     if (e == hipSuccess)
@@ -912,29 +928,30 @@ static hipError_t occupancy_cfg(int* blocks) {
     return e;
 }
 
-#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF, PIPE_OK, ALL_FMT)                              \
-    {ID, LAYOUT, BM, BN, WM, WN, EFF, ALL_FMT, &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, ALL_FMT>, \
+#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF, PIPE_OK, ALL_FMT, KSPEC)                              \
+    {ID, LAYOUT, BM, BN, WM, WN, EFF, ALL_FMT, KSPEC,                                                           \
+     &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, ALL_FMT, KSPEC>,                                     \
      &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>}
 
 static const KernelConfig kConfigs[] = {
     // dense
-    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 2, 1.00, false, false),
-    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 2, 0.90, false, false),
-    DG_CFG(2, kDense, 128, 128, 2, 2, 16, 4, 0.55, false, false),
-    DG_CFG(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false, true),
-    DG_CFG(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true, false),
-    DG_CFG(5, kDense, 256, 256, 4, 2, 16, 2, 1.15, true, true),
+    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 2, 1.00, false, false, false),
+    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 2, 0.90, false, false, false),
+    DG_CFG(2, kDense, 128, 128, 2, 2, 16, 4, 0.55, false, false, false),
+    DG_CFG(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false, true, true),
+    DG_CFG(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true, false, false),
+    DG_CFG(5, kDense, 256, 256, 4, 2, 16, 2, 1.15, true, true, true),
     // contiguous (BLOCK_M = the 128-row segment alignment)
-    DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false, false),
-    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false, true),
-    DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95, true, false),
-    DG_CFG(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false, true),
+    DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false, false, false),
+    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false, true, false),
+    DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95, true, false, false),
+    DG_CFG(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false, true, false),
     // masked
-    DG_CFG(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false, false),
-    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false, true),
-    DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false, false),
-    DG_CFG(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90, false, false),
-    DG_CFG(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, true),
+    DG_CFG(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false, false, false),
+    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false, true, false),
+    DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false, false, false),
+    DG_CFG(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90, false, false, false),
+    DG_CFG(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, true, false),
 };
 
 const KernelConfig* kernel_configs(int* count) {

@@ -34,9 +34,15 @@ struct KernelConfig {
     int bm, bn, wm, wn;
     double eff;            // relative throughput used by the planner
     bool all_formats;      // compiled for E5M2 operands too (else E4M3 only)
+    bool k_specialised;    // has instances with K/128 fixed at compile time (kSpecKBlocks)
     hipError_t (*launch)(const GemmParams&, int grid, hipStream_t);
     hipError_t (*occupancy)(int* blocks_per_cu);
 };
+
+// K/128 values with their own compiled instances (E4M3 operands) in the configurations
+// marked k_specialised: K = 7168 and K = 2048, the hidden and expert widths of the
+// DeepSeek-V3 shapes the workloads use.
+constexpr int kSpecKBlocks[2] = {56, 16};
 
 // Table of compiled configurations (defined in dg_gemm.hip).
 const KernelConfig* kernel_configs(int* count);

@@ -190,8 +190,9 @@ int dg_quantize_fp8_128x128_fmt(const void* x, int x_dtype, long ldx, int rows, 
 int dg_set_kernel_config(int config_id);
 
 /* Enumerate the compiled kernel configurations: for index 0, 1, ... fills
- * out[0..5] = config id, layout, block_m, block_n, waves per workgroup, and 1 if
- * the configuration also runs E5M2 operands (dg_gemm_fp8_nt_fmt) else 0, and
+ * out[0..6] = config id, layout, block_m, block_n, waves per workgroup, 1 if
+ * the configuration also runs E5M2 operands (the _fmt calls) else 0, and 1 if it
+ * has instances compiled for fixed K (see dg_describe_launch) else 0, and
  * returns DG_OK; past the last one returns DG_ERR_INVALID_ARG.  Host only. */
 int dg_kernel_config_info(int index, int* out);
 
@@ -209,10 +210,12 @@ int dg_plan_tiles(int m, int n, int num_units, int blocks_per_unit,
                   const double* eff, int* out);
 
 /* Describe the kernel configuration a call with these sizes would launch, without
- * launching (layout 0 dense, 1 contiguous, 2 masked).  out[0..6] = block_m,
+ * launching (layout 0 dense, 1 contiguous, 2 masked).  out[0..7] = block_m,
  * block_n, waves per workgroup, tiles (upper bound for masked), persistent grid
  * size, config id, row tiles per raster group of the tile order (0 for masked,
- * whose order follows the groups); out must hold 7 ints.  num_cus <= 0 uses
+ * whose order follows the groups), and K/128 if the launch uses an instance
+ * compiled for that K (E4M3 operands; K = 7168 or 2048 in some configurations),
+ * else 0; out must hold 8 ints.  num_cus <= 0 uses
  * dg_get_num_cus().  Needs no device if num_cus > 0 and assumes one resident
  * workgroup per CU for the big shapes. */
 int dg_describe_launch(int layout, int m, int n, int k, int num_groups, int num_cus, int* out);

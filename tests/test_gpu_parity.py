@@ -131,6 +131,30 @@ def test_dense_chained_tiles_all_configs(orc, k):
         dg.dg_set_num_cus(0)
 
 
+@pytest.mark.parametrize("k", [7168, 2048])
+def test_dense_k_specialised_instances(orc, k):
+    """K = 7168 and K = 2048 run instances compiled for that K in the configurations
+    that have them: their output equals the generic configurations' bit for bit and
+    the oracle, on one tile per workgroup and on three workgroups chaining tiles."""
+    dd = W.make_dense(300, 464, k, seed=k + 9)
+    ref = oracle_dense(orc, dd)
+    specs = [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and c["k_specialised"]]
+    generic = [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and not c["k_specialised"]]
+    assert specs and generic
+    base, _ = run_dense(dd, generic[0])
+    check_values(base, ref, f"dense 300x464x{k} generic cfg{generic[0]}")
+    try:
+        for cap in (0, 3):
+            dg.dg_set_num_cus(cap)
+            for cfg in specs:
+                say(f"dense 300x464x{k} cfg={cfg} (K-specialised) cu cap {cap}")
+                out, full = run_dense(dd, cfg)
+                assert np.array_equal(out, base), f"cfg{cfg} cap {cap} differs from the generic kernel"
+                assert np.all(full[:, 464:] == W.SENTINEL_BF16)
+    finally:
+        dg.dg_set_num_cus(0)
+
+
 def test_dense_per_tensor_scaling(orc):
     """Per-tensor scaling is the special case of one value in every scale block: the
     same kernel, checked against the oracle with constant sA and sB."""
