@@ -352,6 +352,38 @@ def test_masked_graph_replay_reads_device_counts(orc):
         check_masked(orc, dict(md, masked_m=np.array(counts, np.int32)), got)
 
 
+def test_masked_maximum_group_count(orc):
+    """1024 groups, the most the masked call takes (the device-side tile enumeration
+    keeps a prefix over the groups in LDS), every count from 0 to the capacity."""
+    groups, cap = 1024, 32
+    mm = [int(x) for x in np.random.default_rng(46).integers(0, cap + 1, size=groups)]
+    mm[0], mm[-1] = cap, cap
+    md = W.make_masked(groups, cap, 32, 256, seed=46, masked_m=mm)
+    say(f"masked {groups} groups, capacity {cap}, n=32 k=256")
+    out = run_masked(md)
+    sentinel = np.full(out.shape, W.SENTINEL_BF16, np.uint16)
+    ref = orc.m_grouped_masked(md["a"], md["sa"], md["b"], md["sb"], md["masked_m"], d_init=sentinel)
+    for g in range(groups):
+        assert np.all(out[g, mm[g]:] == W.SENTINEL_BF16), f"group {g}: a row >= masked_m was written"
+    valid = np.concatenate([out[g, :mm[g]] for g in range(groups)])
+    valid_ref = np.concatenate([ref[g, :mm[g]] for g in range(groups)])
+    check_values(valid, valid_ref, "masked 1024 groups")
+
+
+def test_contiguous_many_small_groups(orc):
+    """300 experts with 0..40 tokens each: most 128-row blocks hold one small segment
+    and its padding."""
+    counts = [int(x) for x in np.random.default_rng(47).integers(0, 41, size=300)]
+    cd = W.make_contiguous(counts, n=48, k=256, seed=47)
+    say(f"contiguous 300 groups, m_total {cd['m_total']}, n=48 k=256")
+    sentinel = np.full((cd["m_total"], 48), W.SENTINEL_BF16, np.uint16)
+    ref = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], cd["m_indices"], d_init=sentinel)
+    valid = cd["m_indices"] >= 0
+    out = run_contiguous(cd)
+    check_values(out[valid], ref[valid], "contiguous 300 groups")
+    assert np.all(out[~valid] == W.SENTINEL_BF16)
+
+
 def test_dense_and_contiguous_graph_replays_match_eager(orc):
     """Dense and contiguous calls captured into one graph give, on every replay (with
     eager work and synchronisation between replays and the inputs changed on the
