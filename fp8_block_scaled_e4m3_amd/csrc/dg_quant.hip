@@ -173,6 +173,26 @@ __device__ __forceinline__ bool any_nan(const float* v, int n) {
 // one decision for the whole wave, so the paths never diverge inside it
 __device__ __forceinline__ bool wave_all(bool b) { return __ballot(!b) == 0; }
 
+// Unsigned 32-bit division by a divisor fixed for the launch, as a multiply-high and
+// shifts (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", 1994, the round-up method): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (t + ((n - t) >> 1)) >> (l - 1) for
+// t = mulhi(n, m) and every 32-bit n; d = 1 uses m = 0 and no shifts.
+struct DivU32 {
+    uint32_t m, s1, s2;
+};
+__host__ DivU32 make_div_u32(uint32_t d) {
+    if (d <= 1) return DivU32{0u, 0u, 0u};
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t m = (((1ull << 32) * ((1ull << l) - d)) / d) + 1;
+    return DivU32{(uint32_t)m, 1u, l - 1};
+}
+__device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 f) {
+    const uint32_t t = __umulhi(n, f.m);
+    return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
 // 1x128: a 128-element row block is read by L = 128/N lanes with one 16-byte load
 // each (the block's bytes are contiguous, so every load instruction is coalesced).
 // A thread handles kRowsPerThread row blocks of one K block, their loads all in
@@ -182,8 +202,8 @@ constexpr int kRowsPerThread = 4;
 
 template <typename T, int FMT>
 __global__ void __launch_bounds__(256)
-quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, uint8_t* __restrict__ q, long ldq,
-                   float* __restrict__ sa, long ld_sa) {
+quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, DivU32 kdiv, uint8_t* __restrict__ q,
+                   long ldq, float* __restrict__ sa, long ld_sa) {
     constexpr int N = Vec<T>::N, L = kQBlock / N, GPW = 256 / L;   // groups of L lanes per workgroup
     const int lg = threadIdx.x % L, grp = threadIdx.x / L;
     // workgroup w handles groups [w*GPW*R, (w+1)*GPW*R); group g = (row, kb) with kb
@@ -195,7 +215,7 @@ quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, uin
     for (int r = 0; r < kRowsPerThread; ++r) {
         const unsigned g = g0 + r * GPW;
         if (g < groups_total) {
-            const unsigned row = g / (unsigned)kblocks, kb = g - row * (unsigned)kblocks;
+            const unsigned row = div_u32(g, kdiv), kb = g - row * (unsigned)kblocks;
             Vec<T>::load(x + (long)row * ldx + kb * kQBlock + lg * N, v[r]);
         }
     }
@@ -210,7 +230,7 @@ quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, uin
             amax = o > amax ? o : amax;
         }
         const float scale = amax == 0.f ? 1.f : amax / Fp8Out<FMT>::kMax;
-        const unsigned row = g / (unsigned)kblocks, kb = g - row * (unsigned)kblocks;
+        const unsigned row = div_u32(g, kdiv), kb = g - row * (unsigned)kblocks;
         const bool fast = wave_all(fast_scale(scale) && !any_nan(v[r], N));
         store_codes<N, FMT>(q + (long)row * ldq + kb * kQBlock + lg * N, v[r], scale, fast);
         if (lg == 0) sa[(long)kb * ld_sa + row] = scale;
@@ -274,6 +294,7 @@ template <int FMT>
 hipError_t launch_1x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq, float* sa,
                         long ld_sa, hipStream_t stream) {
     const int kblocks = k / kQBlock;
+    const DivU32 kdiv = make_div_u32((uint32_t)kblocks);
     const long per_wg = (x_bf16 ? 256 / 16 : 256 / 32) * (long)kRowsPerThread;   // groups per workgroup
     // row chunks small enough for 32-bit group indices inside the kernel
     const long chunk = ((1l << 30) / kblocks) > 0 ? ((1l << 30) / kblocks) : 1;
@@ -282,12 +303,12 @@ hipError_t launch_1x128(const void* x, int x_bf16, long ldx, int rows, int k, ui
         const long blocks = ((long)nr * kblocks + per_wg - 1) / per_wg;
         if (x_bf16)
             hipLaunchKernelGGL((quant_1x128_kernel<uint16_t, FMT>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                               static_cast<const uint16_t*>(x) + r0 * ldx, ldx, nr, kblocks, q + r0 * ldq, ldq,
-                               sa + r0, ld_sa);
+                               static_cast<const uint16_t*>(x) + r0 * ldx, ldx, nr, kblocks, kdiv, q + r0 * ldq,
+                               ldq, sa + r0, ld_sa);
         else
             hipLaunchKernelGGL((quant_1x128_kernel<float, FMT>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                               static_cast<const float*>(x) + r0 * ldx, ldx, nr, kblocks, q + r0 * ldq, ldq, sa + r0,
-                               ld_sa);
+                               static_cast<const float*>(x) + r0 * ldx, ldx, nr, kblocks, kdiv, q + r0 * ldq, ldq,
+                               sa + r0, ld_sa);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
