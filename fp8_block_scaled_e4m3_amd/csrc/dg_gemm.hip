@@ -252,8 +252,23 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             if (step * P >= total_tiles) return false;
             // ---- tile index: XCD-aware hand-out of the linear tile order ----
             int L;
-            if (p.xcd_remap) L = step * P + (w % kXcds) * (P / kXcds) + (w / kXcds);
-            else L = step * P + w;
+            if (p.xcd_remap) {
+                // Each XCD takes a contiguous share of the step's tiles.  Dense: a
+                // partial last round is spread evenly over all eight XCDs rather than
+                // filling the first ones (4-14% faster on 256x256 tiles with 24..248
+                // tiles left; the grouped layouts measured slower with it).
+                const int R = total_tiles - step * P;
+                if (LAYOUT == kDense && R < P) {
+                    const int per = (R + kXcds - 1) / kXcds;
+                    const int j = (w % kXcds) * per + (w / kXcds);
+                    if (w / kXcds >= per || j >= R) continue;   // uniform; idle this step
+                    L = step * P + j;
+                } else {
+                    L = step * P + (w % kXcds) * (P / kXcds) + (w / kXcds);
+                }
+            } else {
+                L = step * P + w;
+            }
             if (L >= total_tiles) continue;   // uniform; this workgroup idles this step
             int g = 0, mb, nb, valid_rows;
             if constexpr (LAYOUT == kMasked) {
