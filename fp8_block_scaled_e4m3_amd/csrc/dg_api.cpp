@@ -102,9 +102,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool valid_fmt(int f) { return f == DG_FMT_E4M3 || f == DG_FMT_E5M2; }
 
 // K/128 of the compile-time-K instance a launch of config c uses, 0 for the generic one
-// (the selection made by the config's launcher: E4M3 operands, K/128 in kSpecKBlocks)
+// (the selection made by the config's launcher: K/128 in kSpecKBlocks, any operand format)
 int specialised_kblocks(const KernelConfig& c, const GemmParams& p) {
-    if (!c.k_specialised || p.fmt != 0) return 0;
+    if (!c.k_specialised) return 0;
     for (int kb : dg::kSpecKBlocks)
         if (p.kblocks == kb) return kb;
     return 0;

@@ -894,40 +894,40 @@ static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-// the E4M3 instance for K/128 == KC (pipelined when KC splits into stage groups)
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, int KC>
-static hipError_t launch_spec(const GemmParams& p, int grid, hipStream_t s) {
-    return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK && KC % NST == 0, 0, KC>(p, grid, s);
-}
-
-// The pipelined variant runs the next tile's first NST blocks as the tail of the
-// current one, which needs the K blocks to split into whole groups of NST.  It is
-// compiled only for the configurations whose registers it fits (PIPE_OK).
-// Configurations with ALL_FMT also have E5M2-operand instances (per-tile variant);
-// the planner gives the others E4M3 operands only.  Configurations with KSPEC have
-// E4M3 instances for each K/128 in kSpecKBlocks, used when the call's K matches.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool ALL_FMT, bool KSPEC>
-static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
+// The instance for operand formats FMT: compiled for K/128 == kSpecKBlocks[i] when the
+// configuration has such instances (KSPEC) and the call's K matches; pipelined (the
+// next tile's first NST blocks run as the tail of the current one) when K/128 splits
+// into whole groups of NST and the configuration fits that variant's registers
+// (PIPE_OK); else the generic per-tile loop.
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool KSPEC, int FMT>
+static hipError_t launch_fmt(const GemmParams& p, int grid, hipStream_t s) {
     static_assert(sizeof(kSpecKBlocks) / sizeof(kSpecKBlocks[0]) == 2, "one branch per specialised K");
     if constexpr (KSPEC) {
-        if (p.fmt == 0 && p.kblocks == kSpecKBlocks[0])
-            return launch_spec<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, kSpecKBlocks[0]>(p, grid, s);
-        if (p.fmt == 0 && p.kblocks == kSpecKBlocks[1])
-            return launch_spec<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, kSpecKBlocks[1]>(p, grid, s);
+        constexpr int K0 = kSpecKBlocks[0], K1 = kSpecKBlocks[1];
+        constexpr bool P0 = PIPE_OK && K0 % NST == 0, P1 = PIPE_OK && K1 % NST == 0;
+        if (p.kblocks == K0) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, P0, FMT, K0>(p, grid, s);
+        if (p.kblocks == K1) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, P1, FMT, K1>(p, grid, s);
     }
+    if constexpr (PIPE_OK) {
+        if (p.kblocks % NST == 0) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, true, FMT>(p, grid, s);
+    }
+    return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, FMT>(p, grid, s);
+}
+
+// Configurations with ALL_FMT have instances for the four operand-format pairs (E5M2 on
+// either side); the planner gives the others E4M3 operands only.
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool ALL_FMT, bool KSPEC>
+static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
     if constexpr (ALL_FMT) {
         switch (p.fmt) {
-            case 1: return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, 1>(p, grid, s);
-            case 2: return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, 2>(p, grid, s);
-            case 3: return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, 3>(p, grid, s);
+            case 1: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, KSPEC, 1>(p, grid, s);
+            case 2: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, KSPEC, 2>(p, grid, s);
+            case 3: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, KSPEC, 3>(p, grid, s);
             default: break;
         }
     }
     if (p.fmt != 0) return hipErrorInvalidValue;
-    if constexpr (PIPE_OK) {
-        if (p.kblocks % NST == 0) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, true, 0>(p, grid, s);
-    }
-    return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, 0>(p, grid, s);
+    return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, KSPEC, 0>(p, grid, s);
 }
 
 template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK>

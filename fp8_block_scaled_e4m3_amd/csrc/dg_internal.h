@@ -39,8 +39,8 @@ struct KernelConfig {
     hipError_t (*occupancy)(int* blocks_per_cu);
 };
 
-// K/128 values with their own compiled instances (E4M3 operands) in the configurations
-// marked k_specialised: K = 7168 and K = 2048, the hidden and expert widths of the
+// K/128 values with their own compiled instances (every operand format the configuration
+// runs) in the configurations marked k_specialised: K = 7168 and K = 2048, the hidden and expert widths of the
 // DeepSeek-V3 shapes the workloads use.
 constexpr int kSpecKBlocks[2] = {56, 16};
 

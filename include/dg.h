@@ -214,8 +214,8 @@ int dg_plan_tiles(int m, int n, int num_units, int blocks_per_unit,
  * block_n, waves per workgroup, tiles (upper bound for masked), persistent grid
  * size, config id, row tiles per raster group of the tile order (0 for masked,
  * whose order follows the groups), and K/128 if the launch uses an instance
- * compiled for that K (E4M3 operands; K = 7168 or 2048 in some configurations),
- * else 0; out must hold 8 ints.  num_cus <= 0 uses
+ * compiled for that K (K = 7168 or 2048 in some configurations), else 0; out
+ * must hold 8 ints.  num_cus <= 0 uses
  * dg_get_num_cus().  Needs no device if num_cus > 0 and assumes one resident
  * workgroup per CU for the big shapes. */
 int dg_describe_launch(int layout, int m, int n, int k, int num_groups, int num_cus, int* out);

@@ -99,6 +99,32 @@ def test_e5m2_large_sampled(orc):
     check_values(out[rows], oracle_fmt(orc, dd, rows), "e5m2xe4m3 2048x4096x2048 sampled rows")
 
 
+@pytest.mark.parametrize("k", [7168, 2048])
+def test_e5m2_k_specialised_instances(orc, k):
+    """At K = 7168 and K = 2048 the E5M2 calls run the instances compiled for that K
+    (pipelined where the K blocks split into stage groups): equal to the oracle, and
+    equal across the configurations carrying them, with one tile per workgroup and
+    with tiles chained on three workgroups."""
+    dd = W.make_dense(300, 464, k, seed=k + 17, a_fmt="e5m2", b_fmt="e4m3")
+    ref = oracle_fmt(orc, dd)
+    specs = [c["id"] for c in dg.dg_kernel_config_info()
+             if c["layout"] == 0 and c["k_specialised"] and c["all_formats"]]
+    assert specs
+    outs = []
+    try:
+        for cap in (0, 3):
+            dg.dg_set_num_cus(cap)
+            for cfg in specs:
+                say(f"dense e5m2xe4m3 300x464x{k} cfg={cfg} cu cap {cap}")
+                out, _ = run_fmt(dd, cfg)
+                check_values(out, ref, f"e5m2 K={k} cfg{cfg} cap {cap}")
+                outs.append(out)
+    finally:
+        dg.dg_set_num_cus(0)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
 def test_e4m3_pair_matches_plain_entry():
     import torch
     dd = W.make_dense(200, 336, 640, seed=3)
