@@ -132,6 +132,22 @@ __device__ __forceinline__ float div_fast(float x, float scale, float r) {
     return __builtin_copysignf(__builtin_fmaf(e, r, q), x);
 }
 
+// fp32(amax / FMAX) (1 when amax is 0), correctly rounded: with the constant r = RN(1/FMAX),
+// q = RN(amax r), the residual amax - q FMAX exact in an FMA and one correction step give
+// the correctly rounded quotient while it is a normal number (the step div_fast uses,
+// here with a fixed divisor; checked against exact rational division on 4e4 values per
+// format across the range).  Smaller or infinite amax take the IEEE division.
+template <int FMT>
+__device__ __forceinline__ float block_scale(float amax) {
+    constexpr float b = Fp8Out<FMT>::kMax;
+    constexpr float r = 1.0f / b;
+    if (amax == 0.f) return 1.f;
+    if (!(amax >= b * 0x1p-125f && amax <= 0x1p127f)) return amax / b;
+    const float q = amax * r;
+    const float e = __builtin_fmaf(-q, b, amax);
+    return __builtin_fmaf(e, r, q);
+}
+
 // N codes of v / scale packed little-endian (4 -> one dword, 8 -> two).  Fast path
 // (every value of the wave finite or infinite but not NaN, the scale in range): the
 // quotient as above and gfx950's FP8 convert (E4M3 or E5M2), which rounds to nearest
@@ -229,7 +245,7 @@ quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, Div
             const float o = __shfl_xor(amax, off, L);
             amax = o > amax ? o : amax;
         }
-        const float scale = amax == 0.f ? 1.f : amax / Fp8Out<FMT>::kMax;
+        const float scale = block_scale<FMT>(amax);
         const unsigned row = div_u32(g, kdiv), kb = g - row * (unsigned)kblocks;
         const bool fast = wave_all(fast_scale(scale) && !any_nan(v[r], N));
         store_codes<N, FMT>(q + (long)row * ldq + kb * kQBlock + lg * N, v[r], scale, fast);
@@ -273,7 +289,7 @@ quant_128x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, u
     amax = s_amax[0];
 #pragma unroll
     for (int w = 1; w < 4; ++w) amax = s_amax[w] > amax ? s_amax[w] : amax;
-    const float scale = amax == 0.f ? 1.f : amax / Fp8Out<FMT>::kMax;
+    const float scale = block_scale<FMT>(amax);
     if (t == 0) sb[(long)rb * kblocks + kb] = scale;
     bool nan = false;
 #pragma unroll
