@@ -4,12 +4,13 @@
 A step is one call of the GEMM on the prefill-like dense workload
 (M=4096, N=7168, K=7168; seeded synthetic E4M3 data with per-1x128 / per-128x128
 fp32 scales, BF16 out) with every input resident in HBM.  Prints ONE JSON line:
-whole-job FP8 TFLOPS, the kernel's roofline position (achieved TFLOP/s from HIP
-events around each launch on the launch stream, against the 5.0 PFLOP/s dense
-FP8 MFMA peak), the CPU oracle timed on a bounded sample of the same workload,
-and -- under "secondary" -- the other workloads (small-M dense, skewed
-contiguous MoE, masked decode) each timed the same way, HBM-bound ones with the
-caches flushed between launches.
+whole-job FP8 TFLOPS, the kernel's roofline position (achieved TFLOP/s from one
+pair of HIP events around the timed steps on the launch stream, against the
+5.0 PFLOP/s dense FP8 MFMA peak), the CPU oracle timed on a bounded sample of the
+same workload, and -- under "secondary" -- the other workloads (small-M dense,
+skewed contiguous MoE, masked decode, the two FP8 casts) each timed the same way,
+HBM-bound ones with cold caches (every launch reads input copies that the
+launches before it have evicted from L2 and the Infinity Cache).
 """
 import argparse
 import hashlib
@@ -47,6 +48,25 @@ def kernel_source_hash() -> str:
 
 def ceil_div(a, b):
     return -(-a // b)
+
+
+def say(*args):
+    print(*args, file=sys.stderr, flush=True)
+
+
+def upload(data: dict) -> dict:
+    """The workload's arrays as GPU tensors (inputs resident in HBM before timing)."""
+    import numpy as np
+    import torch
+    return {key: torch.from_numpy(np.ascontiguousarray(data[key])).to("cuda:0")
+            for key in ("a", "sa", "b", "sb", "m_indices", "masked_m") if key in data}
+
+
+def output_buffer(shape):
+    """BF16 output (as int16 bits), pre-filled with the masked layout's sentinel."""
+    import torch
+    import workloads as W
+    return torch.full(shape, W.SENTINEL_BF16, dtype=torch.int16, device="cuda:0")
 
 
 def algorithmic(w, data):
@@ -90,40 +110,40 @@ def out_shape(w, data):
     return (w.groups, w.max_m, w.n)
 
 
-def warm_up(call, seconds: float = 0.06, cap: int = 400) -> None:
-    """Run `call` back to back for about `seconds` of GPU time (at least 3 times), so the
-    timed launches that follow see the power management settled (see --warmup)."""
-    import torch
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    call()
-    e.record()
-    torch.cuda.synchronize()
-    one = max(s.elapsed_time(e) / 1e3, 1e-6)
-    for _ in range(max(3, min(cap, int(seconds / one)))):
-        call()
-    torch.cuda.synchronize()
+# Input copies an HBM-bound workload cycles through, so that every timed launch reads
+# operands that are in neither the L2 (8 x 4 MB) nor the Infinity Cache (256 MB): each
+# launch's inputs were last touched at least this many bytes of other inputs ago.
+COLD_BYTES = 640 << 20
 
 
-def time_launches(call, iters, flush=None):
-    """Mean kernel time (s) from HIP events recorded around each launch on the
-    stream the kernel is launched on (torch's current stream)."""
+def input_sets(dv: dict, set_bytes: int, cold: bool) -> list:
+    """[dv] for warm-cache timing; else dv plus enough device copies of it that cycling
+    through them evicts each one from the caches before it is read again."""
+    if not cold:
+        return [dv]
+    n = max(2, ceil_div(COLD_BYTES, max(set_bytes, 1)))
+    return [dv] + [{k: v.clone() for k, v in dv.items()} for _ in range(n - 1)]
+
+
+def run_timed(calls: list, warmup: int, steps: int):
+    """`warmup` untimed launches, then `steps` launches back to back between one pair of
+    HIP events recorded on the launch stream (no event between launches: event records
+    there would idle the GPU for ~10 us each).  Launch i runs calls[i % len(calls)].
+    Returns (mean seconds per launch from the events, wall seconds of the timed steps)."""
     import torch
     stream = torch.cuda.current_stream()
-    pairs = []
-    for _ in range(iters):
-        if flush is not None:
-            # evict L2 and the Infinity Cache by reading 512 MB: a read leaves the
-            # caches clean, so the timed kernel pays for no write-back of the flush
-            flush.amax()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record(stream)
-        call()
-        e.record(stream)
-        pairs.append((s, e))
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    ms = [s.elapsed_time(e) for s, e in pairs]
-    return sum(ms) / len(ms) / 1e3, min(ms) / 1e3
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        calls[(warmup + i) % len(calls)]()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1e3 / steps, wall
 
 
 def traffic_for(workload: str):
@@ -167,35 +187,35 @@ CASTS = (("cast_1x128_m4096_k7168_f32", 4096, 7168, 1),
          ("cast_128x128_n7168_k7168_f32", 7168, 7168, 128))
 
 
-def time_casts(iters, flush):
-    """The FP8 casts that feed the GEMM (fp32 in, E4M3 + scales out): HBM-bound."""
+def time_casts(warmup, iters):
+    """The FP8 casts that feed the GEMM (fp32 in, E4M3 + scales out): HBM-bound, timed
+    with cold caches (each launch reads an input copy not read recently)."""
     import torch
 
     import fp8_block_scaled_e4m3_amd as dg
     import workloads as W
-    from tests.gpu_support import say
 
     out = {}
     for cname, rows, k, gran in CASTS:
         say(f"bench: cast {cname}")
-        x = torch.from_numpy(W.make_fp32_operand(rows, k, gran, seed=0)).to("cuda:0")
+        x0 = torch.from_numpy(W.make_fp32_operand(rows, k, gran, seed=0)).to("cuda:0")
+        xs = [t["x"] for t in input_sets({"x": x0}, rows * k * 4, True)]
         q = torch.empty((rows, k), dtype=torch.uint8, device="cuda:0")
         if gran == 1:
-            s_ = torch.empty((k // 128, W.ld_sa_for(rows)), device="cuda:0")
-            c3 = lambda: dg.dg_quantize_fp8_1x128(x, q, s_)
+            s_ = torch.empty((k // 128, dg.dg_get_aligned_ld_sa(rows)), device="cuda:0")
+            calls = [lambda x=x: dg.dg_quantize_fp8_1x128(x, q, s_) for x in xs]
             nsc = (k // 128) * rows
         else:
             s_ = torch.empty((ceil_div(rows, 128), k // 128), device="cuda:0")
-            c3 = lambda: dg.dg_quantize_fp8_128x128(x, q, s_)
+            calls = [lambda x=x: dg.dg_quantize_fp8_128x128(x, q, s_) for x in xs]
             nsc = ceil_div(rows, 128) * (k // 128)
         b3 = rows * k * 4 + rows * k + 4 * nsc
-        for _ in range(3):      # HBM-bound and timed with cold caches: a short warm-up
-            c3()
-        mean_s, _ = time_launches(c3, iters, flush)
+        mean_s, _ = run_timed(calls, warmup, iters)
         out[cname] = {"us": round(mean_s * 1e6, 2), "gbps": round(b3 / mean_s / 1e9, 1),
                       "frac_hbm": round(b3 / mean_s / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm",
-                      "caches_flushed": True, "algorithmic_bytes": b3, "traffic": traffic_for(cname)}
-        del x, q, s_, c3
+                      "cold_caches": True, "input_copies": len(xs), "warmup": warmup, "steps": iters,
+                      "algorithmic_bytes": b3, "traffic": traffic_for(cname)}
+        del x0, xs, q, s_, calls
         torch.cuda.empty_cache()
     return out
 
@@ -203,11 +223,12 @@ def time_casts(iters, flush):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    # Under a sustained FP8 load the chip's power management runs through a transient for
-    # its first ~30 ms (per-launch time up 20-30%, then back down) before it settles; 400
-    # warm-up steps (~70 ms for the headline GEMM) put the timed steps in the settled state.
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=400)
+    # From an idle GPU the chip's power management runs through a transient: a few fast
+    # launches, a throttled stretch ~20-30% slower, then a slow return to the sustained
+    # rate over ~50 ms.  The defaults time steps 6-25, inside that transient (what a
+    # short run sees); --warmup 400 --steps 200 times the sustained state.
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -229,14 +250,12 @@ def main():
 
     import fp8_block_scaled_e4m3_amd as dg
     import workloads as W
-    from tests.gpu_support import say, sentinel_like, upload
 
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     dg.load_library()
     if args.only_casts:
-        flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
-        print(json.dumps({"casts": time_casts(args.secondary_iters, flush)}), flush=True)
+        print(json.dumps({"casts": time_casts(args.warmup, args.secondary_iters)}), flush=True)
         return
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20
@@ -252,7 +271,7 @@ def main():
     say(f"bench: generating {w.name}")
     data = W.make(w)
     dv = upload(data)
-    out = sentinel_like(out_shape(w, data))
+    out = output_buffer(out_shape(w, data))
     call = make_call(w, dv, out)
     flops, byts = algorithmic(w, data)
     plan = dg.dg_describe_launch({"dense": 0, "contiguous": 1, "masked": 2}[w.kind],
@@ -260,26 +279,11 @@ def main():
                                  w.n, w.k, w.groups)
     say(f"bench: plan {plan}; warmup {args.warmup}, timed steps {args.steps}")
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly `steps` steps, synchronised on both sides ----
-    stream = torch.cuda.current_stream()
-    pairs = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record(stream)
-        call()
-        e.record(stream)
-        pairs.append((s, e))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_s = sum(s.elapsed_time(e) for s, e in pairs) / len(pairs) / 1e3
+    # ---- `warmup` untimed steps, then the timed region: exactly `steps` steps back to
+    # back, synchronised on both sides, one HIP event pair around them on the launch stream
+    launch_s, wall = run_timed([call], args.warmup, args.steps)
     ms_per_step = wall / args.steps * 1e3
-    say(f"bench: {ms_per_step:.4f} ms/step wall, {launch_s * 1e6:.1f} us/launch (events)")
+    say(f"bench: {ms_per_step:.4f} ms/step wall, {launch_s * 1e6:.1f} us/launch (events over the timed region)")
 
     if w.kind == "masked":
         value, unit = byts / (ms_per_step / 1e3) / 1e9, "GB/s"
@@ -314,25 +318,28 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_secondary:
+        # The other workloads, each after the same number of untimed launches as the
+        # headline; HBM-bound ones cycle through input copies so that every timed launch
+        # reads from HBM (cold L2 and Infinity Cache), MFMA-bound ones reuse one set.
         sec = {}
-        flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
         for name, ww in W.WORKLOADS.items():
             if name == w.name or name.startswith("dense_m128"):
                 continue
             say(f"bench: secondary {name}")
             d2 = W.make(ww)
             v2 = upload(d2)
-            o2 = sentinel_like(out_shape(ww, d2))
-            c2 = make_call(ww, v2, o2)
+            o2 = output_buffer(out_shape(ww, d2))
             f2, b2 = algorithmic(ww, d2)
-            warm_up(c2)
             hbm_bound = f2 / b2 < PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-            mean_s, best_s = time_launches(c2, args.secondary_iters, flush if hbm_bound else None)
+            sets = input_sets(v2, b2, hbm_bound)
+            calls = [make_call(ww, v, o2) for v in sets]
+            mean_s, _ = run_timed(calls, args.warmup, args.secondary_iters)
             sec[name] = {"us": round(mean_s * 1e6, 2), "tflops": round(f2 / mean_s / 1e12, 2),
                          "gbps": round(b2 / mean_s / 1e9, 1),
                          "frac_mfma": round(f2 / mean_s / 1e12 / PEAK_FP8_TFLOPS, 4),
                          "frac_hbm": round(b2 / mean_s / 1e9 / PEAK_HBM_GBS, 4),
-                         "bound": "hbm" if hbm_bound else "mfma", "caches_flushed": hbm_bound,
+                         "bound": "hbm" if hbm_bound else "mfma", "cold_caches": hbm_bound,
+                         "input_copies": len(sets), "warmup": args.warmup, "steps": args.secondary_iters,
                          "algorithmic_flops": f2, "algorithmic_bytes": b2,
                          "traffic": traffic_for(name)}
             if ww.kind == "masked":
@@ -343,15 +350,14 @@ def main():
                 for cap in CU_CAPS:
                     dg.dg_set_num_cus(cap)
                     try:
-                        c2()
-                        cs, _ = time_launches(c2, args.secondary_iters, flush)
+                        cs, _ = run_timed(calls, args.warmup, args.secondary_iters)
                     finally:
                         dg.dg_set_num_cus(0)
                     capped[str(cap)] = {"us": round(cs * 1e6, 2), "gbps": round(b2 / cs / 1e9, 1)}
                 sec[name]["cu_capped"] = capped
-            del d2, v2, o2, c2
+            del d2, v2, o2, sets, calls
             torch.cuda.empty_cache()
-        sec.update(time_casts(args.secondary_iters, flush))
+        sec.update(time_casts(args.warmup, args.secondary_iters))
         result["secondary"] = sec
 
     if not args.no_cpu_baseline and w.kind == "dense":

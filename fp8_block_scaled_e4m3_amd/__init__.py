@@ -84,6 +84,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_plan_tiles.restype = I
     lib.dg_describe_launch.argtypes = [I, I, I, I, I, I, P]
     lib.dg_describe_launch.restype = I
+    lib.dg_get_aligned_ld_sa.argtypes = [L]
+    lib.dg_get_aligned_ld_sa.restype = L
+    lib.dg_transform_sa_mn_major.argtypes = [P, L, P, L, I, I, I, P]
+    lib.dg_transform_sa_mn_major.restype = I
+    lib.dg_check_contiguous_layout.argtypes = [P, I, I, P]
+    lib.dg_check_contiguous_layout.restype = I
     _lib = lib
     return lib
 
@@ -194,7 +200,7 @@ def dg_gemm_fp8_nt_fmt(a, sa, b, sb, d, a_fmt=None, b_fmt=None, stream=None) -> 
     fa, fb = _fmt_of(a, a_fmt), _fmt_of(b, b_fmt)
     if b.shape[1] != k or tuple(d.shape) != (m, n):
         raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, d {tuple(d.shape)}")
-    if sa.shape[0] != -(-k // 128) or sb.shape[1] != -(-k // 128) or sb.shape[0] != -(-n // 128):
+    if sa.shape[0] != -(-k // 128) or sa.shape[1] < m or sb.shape[1] != -(-k // 128) or sb.shape[0] != -(-n // 128):
         raise ValueError(f"scale shape mismatch: sa {tuple(sa.shape)}, sb {tuple(sb.shape)}")
     if not sb.is_contiguous():
         raise ValueError("sb must be contiguous")
@@ -226,7 +232,7 @@ def dg_m_grouped_gemm_fp8_contiguous_fmt(a, sa, b, sb, d, m_indices, a_fmt=None,
             raise ValueError(f"{nm} must be contiguous")
     if tuple(d.shape) != (m_total, n) or b.shape[2] != k or m_indices.shape[0] != m_total:
         raise ValueError("shape mismatch")
-    if tuple(sb.shape) != (g, -(-n // 128), -(-k // 128)) or sa.shape[0] != -(-k // 128):
+    if tuple(sb.shape) != (g, -(-n // 128), -(-k // 128)) or sa.shape[0] != -(-k // 128) or sa.shape[1] < m_total:
         raise ValueError("scale shape mismatch")
     _check(load_library().dg_m_grouped_gemm_fp8_contiguous_fmt(pa, psa, sa.stride(0), pb, psb, pd, pmi,
                                                                m_total, n, k, g, fa, fb, _stream(stream)),
@@ -314,6 +320,56 @@ def dg_quantize_fp8_128x128_fmt(x, q, sb, q_fmt=None, stream=None) -> None:
                                                       _stream(stream)), "dg_quantize_fp8_128x128_fmt")
 
 
+def dg_get_aligned_ld_sa(rows: int) -> int:
+    """Smallest leading dimension of an MN-major sA for ``rows`` rows that the GEMMs and
+    the 1x128 cast accept (rows rounded up to a multiple of 4)."""
+    v = int(load_library().dg_get_aligned_ld_sa(int(rows)))
+    if v < 0:
+        raise DGError(v, "dg_get_aligned_ld_sa")
+    return v
+
+
+def dg_transform_sa_mn_major(sa_in, sa_out=None, stream=None):
+    """Per-row scales stored row-major, ``sa_in`` [rows, K/128] (or [G, rows, K/128]),
+    to the MN-major layout the GEMMs read, [K/128, ld_sa] (or [G, K/128, ld_sa]) with
+    ld_sa = dg_get_aligned_ld_sa(rows).  Returns ``sa_out`` (allocated by torch when
+    not given; its padding columns are then zero)."""
+    import torch
+    squeeze = sa_in.dim() == 2
+    x = sa_in.unsqueeze(0) if squeeze else sa_in
+    _dev(x, "sa_in", _f32(), 3)
+    g, rows, kb = x.shape
+    if g > 1 and x.stride(0) != rows * x.stride(1):
+        raise ValueError("sa_in groups must be stacked contiguously ([G, rows, ld_in] with stride rows*ld_in)")
+    ld = dg_get_aligned_ld_sa(rows)
+    if sa_out is None:
+        sa_out = torch.zeros((g, kb, ld) if not squeeze else (kb, ld), dtype=torch.float32, device=x.device)
+    y = sa_out.unsqueeze(0) if squeeze else sa_out
+    _dev(y, "sa_out", _f32(), 3)
+    if tuple(y.shape[:2]) != (g, kb) or y.shape[2] < rows or not y.is_contiguous():
+        raise ValueError(f"sa_out must be contiguous [{g}, {kb}, >= {rows}], got {tuple(y.shape)}")
+    _check(load_library().dg_transform_sa_mn_major(ctypes.c_void_p(x.data_ptr()), x.stride(1),
+                                                   ctypes.c_void_p(y.data_ptr()), y.shape[2], rows, kb, g,
+                                                   _stream(stream)), "dg_transform_sa_mn_major")
+    return sa_out
+
+
+def dg_check_contiguous_layout(m_indices, num_groups: int):
+    """Check the contiguous layout's precondition on a host copy of m_indices (numpy or
+    CPU tensor).  Returns None when it holds, else the first offending row."""
+    import numpy as np
+    mi = np.ascontiguousarray(np.asarray(m_indices, dtype=np.int32))
+    bad = ctypes.c_int(-1)
+    r = load_library().dg_check_contiguous_layout(mi.ctypes.data_as(ctypes.c_void_p), int(mi.size),
+                                                  int(num_groups), ctypes.byref(bad))
+    if r == DG_OK:
+        return None
+    if bad.value < 0:
+        raise DGError(r, "dg_check_contiguous_layout")
+    return int(bad.value)
+
+
+# ---- tuning and introspection hooks (dg_tuning.h: outside the library's contract)
 def dg_set_kernel_config(config_id: int) -> None:
     """Pin a kernel configuration id for its layout (-1: automatic planning again)."""
     _check(load_library().dg_set_kernel_config(int(config_id)), "dg_set_kernel_config")
@@ -359,5 +415,8 @@ __all__ = [
     "dg_get_m_alignment", "dg_set_num_cus", "dg_get_num_cus",
     "dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "DG_FMT_E4M3", "DG_FMT_E5M2", "dg_m_grouped_gemm_fp8_contiguous", "dg_m_grouped_gemm_fp8_masked",
     "dg_m_grouped_gemm_fp8_contiguous_fmt", "dg_m_grouped_gemm_fp8_masked_fmt",
-    "dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_fmt", "dg_quantize_fp8_128x128_fmt", "dg_set_kernel_config", "dg_kernel_config_info", "dg_plan_tiles", "dg_describe_launch",
+    "dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_fmt",
+    "dg_quantize_fp8_128x128_fmt", "dg_get_aligned_ld_sa", "dg_transform_sa_mn_major",
+    "dg_check_contiguous_layout", "dg_plan_tiles",
+    "dg_set_kernel_config", "dg_kernel_config_info", "dg_describe_launch",
 ]

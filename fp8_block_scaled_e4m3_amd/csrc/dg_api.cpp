@@ -13,6 +13,7 @@
 #include <mutex>
 
 #include "../../include/dg.h"
+#include "../../include/dg_tuning.h"
 #include "dg_internal.h"
 
 namespace {
@@ -27,7 +28,9 @@ constexpr int kXcds = 8;
 constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_cu_cap{0};
-std::atomic<int> g_forced_cfg[3] = {{-1}, {-1}, {-1}};   // per layout: index into the table
+// dg_set_kernel_config: per layout, an index into the config table, or -1.  Per
+// thread, so that pinning a configuration never re-plans another thread's calls.
+thread_local int g_forced_cfg[3] = {-1, -1, -1};
 
 struct DeviceInfo {
     bool init = false;
@@ -116,6 +119,8 @@ int specialised_kblocks(const KernelConfig& c, const GemmParams& p) {
 // whose offsets would not fit are refused rather than wrapped.
 bool offsets_fit(long lda, long ldb, long ld_sa, int k) {
     const long lim = 0xFFFFFFFFl;
+    // (each bound checked before the product it guards, so no product overflows)
+    if (lda > lim / 256 || ldb > lim / 256 || ld_sa > lim / 4) return false;
     return 256 * lda + k <= lim && 256 * ldb + k <= lim && (long)(k / kKBlock) * ld_sa * 4 + 4096 <= lim;
 }
 
@@ -162,7 +167,7 @@ int choose_config(int layout, int m, int n, int num_groups, int fmt, int num_uni
                   int max_m_hint) {
     int count = 0;
     const KernelConfig* cfgs = dg::kernel_configs(&count);
-    const int forced = g_forced_cfg[layout].load();
+    const int forced = g_forced_cfg[layout];
     if (forced >= 0 && forced < count) return (fmt == 0 || cfgs[forced].all_formats) ? forced : -1;
     int best = -1;
     double best_cost = 0.0;
@@ -284,14 +289,14 @@ int dg_get_num_cus(void) {
 
 int dg_set_kernel_config(int config_id) {
     if (config_id == -1) {
-        for (auto& f : g_forced_cfg) f.store(-1);
+        for (auto& f : g_forced_cfg) f = -1;
         return DG_OK;
     }
     int count = 0;
     const KernelConfig* cfgs = dg::kernel_configs(&count);
     for (int i = 0; i < count; ++i) {
         if (cfgs[i].id == config_id) {
-            g_forced_cfg[cfgs[i].layout].store(i);
+            g_forced_cfg[cfgs[i].layout] = i;
             return DG_OK;
         }
     }
@@ -306,7 +311,9 @@ static int check_quant(const void* x, int x_dtype, long ldx, int rows, int k, co
     if (!x || !q || !s) return DG_ERR_INVALID_ARG;
     if (ldx < k || ldq < k) return DG_ERR_INVALID_ARG;
     const long esz = x_dtype == DG_DTYPE_F32 ? 4 : 2;
-    if (!aligned16(x) || (ldx * esz) % 16 || (reinterpret_cast<uintptr_t>(q) & 7u) || ldq % 8 ||
+    // the kernels address row r at r * ld elements: keep every such offset in 63 bits
+    if (ldx > LONG_MAX / 4 / rows || ldq > LONG_MAX / 4 / rows) return DG_ERR_UNSUPPORTED;
+    if (!aligned16(x) || ldx % (16 / esz) || (reinterpret_cast<uintptr_t>(q) & 7u) || ldq % 8 ||
         (reinterpret_cast<uintptr_t>(s) & 3u))
         return DG_ERR_MISALIGNED;
     return DG_OK;
@@ -318,6 +325,8 @@ int dg_quantize_fp8_1x128_fmt(const void* x, int x_dtype, long ldx, int rows, in
     const int st = check_quant(x, x_dtype, ldx, rows, k, q, ldq, sa);
     if (st != DG_OK || rows == 0) return st;
     if (ld_sa < rows) return DG_ERR_INVALID_ARG;
+    // sA exactly as the GEMMs take it: 16-byte aligned rows of the MN-major layout
+    if (ld_sa % 4 || !aligned16(sa)) return DG_ERR_MISALIGNED;
     if (dg::launch_quant_1x128(x, x_dtype == DG_DTYPE_BF16, ldx, rows, k, static_cast<uint8_t*>(q), ldq, sa, ld_sa,
                                q_fmt == DG_FMT_E5M2, static_cast<hipStream_t>(stream)) != hipSuccess) {
         (void)hipGetLastError();
@@ -347,6 +356,52 @@ int dg_quantize_fp8_128x128_fmt(const void* x, int x_dtype, long ldx, int rows, 
 int dg_quantize_fp8_128x128(const void* x, int x_dtype, long ldx, int rows, int k, void* q, long ldq, float* sb,
                             void* stream) {
     return dg_quantize_fp8_128x128_fmt(x, x_dtype, ldx, rows, k, q, ldq, sb, DG_FMT_E4M3, stream);
+}
+
+long dg_get_aligned_ld_sa(long rows) {
+    if (rows < 0) return DG_ERR_INVALID_ARG;
+    if (rows > LONG_MAX - 3) return DG_ERR_UNSUPPORTED;
+    return (rows + 3) / 4 * 4;
+}
+
+int dg_transform_sa_mn_major(const float* sa_in, long ld_in, float* sa_out, long ld_sa, int rows, int kblocks,
+                             int groups, void* stream) {
+    if (rows < 0 || kblocks < 0 || groups < 1) return DG_ERR_INVALID_ARG;
+    if (rows == 0 || kblocks == 0) return DG_OK;
+    if (!sa_in || !sa_out || ld_in < kblocks || ld_sa < rows) return DG_ERR_INVALID_ARG;
+    if (ld_sa % 4 || !aligned16(sa_out) || (reinterpret_cast<uintptr_t>(sa_in) & 3u)) return DG_ERR_MISALIGNED;
+    if (ld_in > INT_MAX || ld_sa > INT_MAX || (long)rows * ld_in > INT_MAX || (long)kblocks * ld_sa > INT_MAX ||
+        groups > 65535 || kblocks > 65535 * 32)
+        return DG_ERR_UNSUPPORTED;
+    if (dg::launch_sa_mn_major(sa_in, ld_in, sa_out, ld_sa, rows, kblocks, groups,
+                               static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return DG_ERR_HIP;
+    }
+    return DG_OK;
+}
+
+int dg_check_contiguous_layout(const int* m_indices, int m_total, int num_groups, int* bad_row) {
+    if (bad_row) *bad_row = -1;
+    if (m_total < 0 || num_groups < 1 || (m_total > 0 && !m_indices)) return DG_ERR_INVALID_ARG;
+    if (m_total % kMAlign != 0) {
+        if (bad_row) *bad_row = m_total;
+        return DG_ERR_INVALID_ARG;
+    }
+    for (int b = 0; b < m_total; b += kMAlign) {
+        const int g = m_indices[b];
+        for (int r = b; r < b + kMAlign; ++r) {
+            const int v = m_indices[r];
+            // entries are a group or -1; a block's group is that of its first row, and
+            // every other row of the block is that group or padding
+            const bool ok = v >= -1 && v < num_groups && (v == -1 || v == g);
+            if (!ok) {
+                if (bad_row) *bad_row = r;
+                return DG_ERR_INVALID_ARG;
+            }
+        }
+    }
+    return DG_OK;
 }
 
 int dg_kernel_config_info(int index, int* out) {
@@ -417,7 +472,8 @@ int dg_gemm_fp8_nt_fmt(const void* a, long lda, const float* sa, long ld_sa, con
     if (!a || !sa) return DG_ERR_INVALID_ARG;
     if (lda < k || ldb < k || ldd < n || ld_sa < m) return DG_ERR_INVALID_ARG;
     if (!aligned16(a) || !aligned16(sa) || lda % 16 || ldb % 16 || ldd % 8 || ld_sa % 4) return DG_ERR_MISALIGNED;
-    if ((long)m * lda > LONG_MAX / 2 || !offsets_fit(lda, ldb, ld_sa, k)) return DG_ERR_UNSUPPORTED;
+    if (!offsets_fit(lda, ldb, ld_sa, k) || (long)m * lda > LONG_MAX / 2 || ldd > LONG_MAX / 4 / m)
+        return DG_ERR_UNSUPPORTED;
     GemmParams p{};
     p.a = static_cast<const uint8_t*>(a);
     p.lda = lda;

@@ -235,7 +235,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // copies, scales and epilogue need, all wave-uniform ----
     // (rows [row_lo, row_hi) of the tile are this pass's valid rows)
     struct Tile {
-        int m0, row_lo, row_hi, wcol0;
+        int m0, row_lo, row_hi, wcol0, grp;
         unsigned hi_mask;
         int sb_off[NSB];
         bool active;
@@ -349,6 +349,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         const int g = pass == 0 ? pg[0] : pg[1];
         const int m0 = st_m0, n0 = st_n0, valid_rows = st_vr;
         t.m0 = m0;
+        t.grp = g;
         t.row_lo = pass == 0 ? plo[0] : plo[1];
         t.row_hi = min(pass == 0 ? phi[0] : phi[1], valid_rows);
         const uint8_t* a_tile = a_ptr + (LAYOUT == kMasked ? (long)g * p.a_gstride : 0) + (long)m0 * p.lda;
@@ -390,6 +391,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // no tile: its copies read nothing (every lane is out of range) and write zeros
     auto null_tile = [&](Tile& t) DG_INLINE {
         t.m0 = t.row_lo = t.row_hi = t.wcol0 = 0;
+        t.grp = -1;
         t.hi_mask = 0;
 #pragma unroll
         for (int i = 0; i < NSB; ++i) t.sb_off[i] = 0;
@@ -823,7 +825,9 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 const int lr = wm * WTM + fm * MF + lsub;     // row inside the tile
                 bool row_ok = lr >= cur.row_lo && lr < cur.row_hi;
                 if constexpr (LAYOUT == kContiguous) {
-                    if (row_ok) row_ok = p.m_indices[cur.m0 + lr] >= 0;
+                    // only rows of this pass's group: padding (-1) and entries that
+                    // break the one-group-per-segment-block rule are not written
+                    if (row_ok) row_ok = p.m_indices[cur.m0 + lr] == cur.grp;
                 }
                 uint16_t* drow = cur.d_tile + (long)(row_ok ? lr : 0) * p.ldd;
                 if constexpr (MF == 16) {
@@ -946,28 +950,9 @@ static hipError_t occupancy_cfg(int* blocks) {
 #define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF, PIPE_OK, ALL_FMT, KSPEC)                              \
     {ID, LAYOUT, BM, BN, WM, WN, EFF, ALL_FMT, KSPEC,                                                           \
      &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, ALL_FMT, KSPEC>,                                     \
-     &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>}
+     &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>},
 
-static const KernelConfig kConfigs[] = {
-    // dense
-    DG_CFG(0, kDense, 256, 224, 4, 2, 16, 2, 1.00, false, false, false),
-    DG_CFG(1, kDense, 256, 224, 8, 1, 32, 2, 0.90, false, false, false),
-    DG_CFG(2, kDense, 128, 128, 2, 2, 16, 4, 0.55, false, false, false),
-    DG_CFG(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false, true, true),
-    DG_CFG(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true, false, false),
-    DG_CFG(5, kDense, 256, 256, 4, 2, 16, 2, 1.15, true, true, true),
-    // contiguous (BLOCK_M = the 128-row segment alignment)
-    DG_CFG(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false, false, false),
-    DG_CFG(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false, true, false),
-    DG_CFG(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95, true, false, false),
-    DG_CFG(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false, true, false),
-    // masked
-    DG_CFG(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false, false, false),
-    DG_CFG(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false, true, false),
-    DG_CFG(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false, false, false),
-    DG_CFG(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90, false, false, false),
-    DG_CFG(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, true, false),
-};
+static const KernelConfig kConfigs[] = {DG_CONFIG_TABLE(DG_CFG)};
 
 const KernelConfig* kernel_configs(int* count) {
     *count = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));

@@ -44,6 +44,30 @@ struct KernelConfig {
 // DeepSeek-V3 shapes the workloads use.
 constexpr int kSpecKBlocks[2] = {56, 16};
 
+// The compiled tile configurations: X(id, layout, BLOCK_M, BLOCK_N, waves along M, waves
+// along N, MFMA tile (16 or 32), LDS stages, relative throughput for the planner,
+// pipelined variant fits the registers, E5M2 instances, compile-time-K instances).
+// dg_gemm.hip instantiates a kernel for each row; the planner reads the same rows.
+#define DG_CONFIG_TABLE(X)                                                   \
+    /* dense */                                                              \
+    X(0, kDense, 256, 224, 4, 2, 16, 2, 1.00, false, false, false)          \
+    X(1, kDense, 256, 224, 8, 1, 32, 2, 0.90, false, false, false)          \
+    X(2, kDense, 128, 128, 2, 2, 16, 4, 0.55, false, false, false)          \
+    X(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false, true, true)             \
+    X(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true, false, false)           \
+    X(5, kDense, 256, 256, 4, 2, 16, 2, 1.15, true, true, true)             \
+    /* contiguous (BLOCK_M = the 128-row segment alignment, or two of them) */ \
+    X(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false, false, false)    \
+    X(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false, true, false)     \
+    X(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95, true, false, false)     \
+    X(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false, true, false)     \
+    /* masked */                                                             \
+    X(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false, false, false)        \
+    X(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false, true, false)         \
+    X(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false, false, false)        \
+    X(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90, false, false, false)        \
+    X(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, true, false)
+
 // Table of compiled configurations (defined in dg_gemm.hip).
 const KernelConfig* kernel_configs(int* count);
 
@@ -53,5 +77,8 @@ hipError_t launch_quant_1x128(const void* x, int x_bf16, long ldx, int rows, int
                               long ld_sa, int q_e5m2, hipStream_t stream);
 hipError_t launch_quant_128x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq,
                                 float* sb, int q_e5m2, hipStream_t stream);
+// sA from row-major [groups][rows][ld_in] to MN-major [groups][kblocks][ld_sa] (dg_quant.hip).
+hipError_t launch_sa_mn_major(const float* in, long ld_in, float* out, long ld_sa, int rows, int kblocks, int groups,
+                              hipStream_t stream);
 
 }  // namespace dg

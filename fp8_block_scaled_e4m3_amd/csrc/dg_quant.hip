@@ -12,79 +12,27 @@
 // at +-448 (the format's largest finite value), NaN -> 0x7F, sign of zero kept.
 // E5M2 output (the blog's other FP8 format, hnwysp.cn section 2.3) is the same with
 // 57344, E5M2's largest finite value, in place of 448.
-// Both divisions are IEEE-correctly-rounded fp32 divisions, so the codes are a
+// Both quotients are the correctly rounded fp32 ones (what an IEEE division gives;
+// dg_cast_math.h reaches them without one on the fast path), so the codes are a
 // deterministic function of the input.  Each kernel reads its input once.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dg_cast_math.h"
 #include "dg_internal.h"
 
 namespace dg {
 
 namespace {
 
+using namespace castmath;
+
 constexpr int kQBlock = 128;
-constexpr float kE4M3Max = 448.0f;
-constexpr float kE5M2Max = 57344.0f;
 
 __device__ __forceinline__ float load_elem(const float* p) { return *p; }
 __device__ __forceinline__ float load_elem(const uint16_t* p) {
     return __uint_as_float(((uint32_t)*p) << 16);   // bf16 -> fp32 is exact
 }
-
-// E4M3 code of an fp32 value, round to nearest even, saturating.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-    const uint32_t bits = __float_as_uint(y);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const float a = fabsf(y);
-    if (!(a == a)) return 0x7Fu;                       // NaN
-    if (a >= kE4M3Max) return sign | 0x7Eu;            // saturate at 448
-    if (a < 0.015625f) {                               // below 2^-6: multiples of 2^-9
-        const float q = __builtin_rintf(a * 512.0f);   // exact scaling, RNE (q <= 8)
-        return sign | (uint32_t)q;                     // q == 8 is the smallest normal
-    }
-    // normal range: keep 3 of 23 mantissa bits, ties to even, carry into the exponent
-    const uint32_t ab = bits & 0x7FFFFFFFu;
-    const uint32_t rounded = ab + 0x7FFFFu + ((ab >> 20) & 1u);
-    return sign | ((rounded >> 20) - (120u << 3));     // rebias exponent 127 -> 7
-}
-
-// E5M2 code of an fp32 value, round to nearest even, saturating (bias 15, two
-// stored mantissa bits, subnormals are the multiples of 2^-16 below 2^-14).
-__device__ __forceinline__ uint32_t e5m2_code(float y) {
-    const uint32_t bits = __float_as_uint(y);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const float a = fabsf(y);
-    if (!(a == a)) return 0x7Fu;                       // NaN
-    if (a >= kE5M2Max) return sign | 0x7Bu;            // saturate at 57344
-    if (a < 0x1p-14f) {                                // below 2^-14: multiples of 2^-16
-        const float q = __builtin_rintf(a * 65536.0f); // exact scaling, RNE (q <= 4)
-        return sign | (uint32_t)q;                     // q == 4 is the smallest normal
-    }
-    // normal range: keep 2 of 23 mantissa bits, ties to even, carry into the exponent
-    const uint32_t ab = bits & 0x7FFFFFFFu;
-    const uint32_t rounded = ab + 0xFFFFFu + ((ab >> 21) & 1u);
-    return sign | ((rounded >> 21) - (112u << 2));     // rebias exponent 127 -> 15
-}
-
-// Output format FMT: 0 = E4M3, 1 = E5M2.
-template <int FMT> struct Fp8Out;
-template <> struct Fp8Out<0> {
-    static constexpr float kMax = kE4M3Max;
-    static __device__ __forceinline__ uint32_t code(float y) { return e4m3_code(y); }
-    template <bool HI>
-    static __device__ __forceinline__ int pack(float a, float b, int old) {
-        return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
-    }
-};
-template <> struct Fp8Out<1> {
-    static constexpr float kMax = kE5M2Max;
-    static __device__ __forceinline__ uint32_t code(float y) { return e5m2_code(y); }
-    template <bool HI>
-    static __device__ __forceinline__ int pack(float a, float b, int old) {
-        return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
-    }
-};
 
 // One 16-byte load: 4 fp32 or 8 bf16 values, widened to fp32 (bf16 -> fp32 is exact).
 template <typename T> struct Vec;
@@ -116,44 +64,6 @@ __device__ __forceinline__ float amax_of(const float* v, int n, float amax) {
         amax = m > amax ? m : amax;              // a NaN never raises the maximum
     }
     return amax;
-}
-
-// Scales whose reciprocal is a normal number: the fast quotient below is exact there.
-__device__ __forceinline__ bool fast_scale(float scale) { return scale > 0x1p-125f && scale < 0x1p125f; }
-
-// RN(1/s) for 2^-125 < s < 2^125 (the fast path's scales): one FMA Newton step from the
-// hardware reciprocal.  An exhaustive run on gfx950 over every fp32 significand at every
-// exponent of that range matched the IEEE division bit for bit.
-__device__ __forceinline__ float rcp_exact(float s) {
-    const float y = __builtin_amdgcn_rcpf(s);
-    return __builtin_fmaf(__builtin_fmaf(-s, y, 1.0f), y, y);
-}
-
-// x / scale correctly rounded, given r = RN(1/scale) with scale and r normal:
-// q = RN(x*r) is within one ulp of the quotient, the residual x - q*scale is exact
-// in a fused multiply-add, and one correction step rounds correctly (Markstein's
-// theorem for radix-2 division).  The quotient has the sign of x (scale > 0); the
-// copysign keeps it for x = -0, where the correction step would return +0.
-__device__ __forceinline__ float div_fast(float x, float scale, float r) {
-    const float q = x * r;
-    const float e = __builtin_fmaf(-q, scale, x);
-    return __builtin_copysignf(__builtin_fmaf(e, r, q), x);
-}
-
-// fp32(amax / FMAX) (1 when amax is 0), correctly rounded: with the constant r = RN(1/FMAX),
-// q = RN(amax r), the residual amax - q FMAX exact in an FMA and one correction step give
-// the correctly rounded quotient while it is a normal number (the step div_fast uses,
-// here with a fixed divisor; checked against exact rational division on 4e4 values per
-// format across the range).  Smaller or infinite amax take the IEEE division.
-template <int FMT>
-__device__ __forceinline__ float block_scale(float amax) {
-    constexpr float b = Fp8Out<FMT>::kMax;
-    constexpr float r = 1.0f / b;
-    if (amax == 0.f) return 1.f;
-    if (!(amax >= b * 0x1p-125f && amax <= 0x1p127f)) return amax / b;
-    const float q = amax * r;
-    const float e = __builtin_fmaf(-q, b, amax);
-    return __builtin_fmaf(e, r, q);
 }
 
 // N codes of v / scale packed little-endian (4 -> one dword, 8 -> two).  Fast path
@@ -310,6 +220,34 @@ quant_128x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, u
     }
 }
 
+// sA layout transform: per-row scales stored row-major, in[g][row][kb] (row stride
+// ld_in), to the MN-major layout the GEMMs read, out[g][kb][row] (row stride ld_sa) --
+// the README's utility that returns the LHS scales column-major with an aligned leading
+// dimension.  A 32 x 32 tile goes through LDS so that both the reads (along kb) and the
+// writes (along rows) are contiguous; the padding columns [rows, ld_sa) are not written.
+constexpr int kTT = 32;
+
+__global__ void __launch_bounds__(256)
+sa_mn_major_kernel(const float* __restrict__ in, long ld_in, float* __restrict__ out, long ld_sa, int rows,
+                   int kblocks) {
+    __shared__ float tile[kTT][kTT + 1];
+    const int r0 = blockIdx.x * kTT, k0 = blockIdx.y * kTT, g = blockIdx.z;
+    const float* src = in + (long)g * rows * ld_in;
+    float* dst = out + (long)g * kblocks * ld_sa;
+    const int tx = threadIdx.x % kTT, ty = threadIdx.x / kTT;   // 32 x 8 threads
+#pragma unroll
+    for (int i = 0; i < kTT; i += 8) {
+        const int r = r0 + ty + i, k = k0 + tx;
+        if (r < rows && k < kblocks) tile[ty + i][tx] = src[(long)r * ld_in + k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kTT; i += 8) {
+        const int k = k0 + ty + i, r = r0 + tx;
+        if (r < rows && k < kblocks) dst[(long)k * ld_sa + r] = tile[tx][ty + i];
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -359,6 +297,13 @@ hipError_t launch_quant_1x128(const void* x, int x_bf16, long ldx, int rows, int
                               long ld_sa, int q_e5m2, hipStream_t stream) {
     return q_e5m2 ? launch_1x128<1>(x, x_bf16, ldx, rows, k, q, ldq, sa, ld_sa, stream)
                   : launch_1x128<0>(x, x_bf16, ldx, rows, k, q, ldq, sa, ld_sa, stream);
+}
+
+hipError_t launch_sa_mn_major(const float* in, long ld_in, float* out, long ld_sa, int rows, int kblocks, int groups,
+                              hipStream_t stream) {
+    const dim3 grid((unsigned)((rows + kTT - 1) / kTT), (unsigned)((kblocks + kTT - 1) / kTT), (unsigned)groups);
+    hipLaunchKernelGGL(sa_mn_major_kernel, grid, dim3(256), 0, stream, in, ld_in, out, ld_sa, rows, kblocks);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_128x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq,

@@ -33,11 +33,15 @@
  *    count (else DG_ERR_MISALIGNED / DG_ERR_INVALID_ARG).
  *  - Size limits (else DG_ERR_UNSUPPORTED): 256 * lda + K and 256 * ldb + K below
  *    2^32 bytes, (K / 128) * ld_sa * 4 + 4096 below 2^32 bytes (for the grouped
- *    layouts lda = ldb = K), and fewer than 2^30 output tiles; the kernels address
- *    each tile's operands through 32-bit offsets from the tile's first row.
+ *    layouts lda = ldb = K), M * ldd * 4 below 2^63, and fewer than 2^30 output tiles;
+ *    the kernels address each tile's operands through 32-bit offsets from the tile's
+ *    first row.
  *  - M == 0 (or all masked_m == 0) is a valid no-op.
  *  - Calls on distinct streams may run concurrently; the only library state is the
  *    CU cap (dg_set_num_cus) and a per-device property cache.
+ *  - Tuning and introspection hooks that are not part of this contract (pinning a
+ *    tile configuration, listing the compiled ones, describing a launch) are declared
+ *    in dg_tuning.h.
  */
 #ifndef DG_H
 #define DG_H
@@ -108,9 +112,11 @@ int dg_gemm_fp8_nt_fmt(const void* a, long lda, const float* sa, long ld_sa,
  *   b  [G][n][k]     E4M3          sb [G][ceil(n/128)][k/128] fp32
  *   d  [m_total][n]  BF16 bits
  *   m_indices [m_total] int32: the group of each row, or -1 for a padding row.
- * Device-side precondition (not checked on the host): within each aligned 128-row
- * block every non-negative entry is the same group and the block's first row is
- * not padding unless the whole block is.  Rows with -1 are not written.
+ * Device-side precondition (not checked by this call, which never reads m_indices on
+ * the host; dg_check_contiguous_layout checks a host copy): within each aligned
+ * 128-row block every non-negative entry is the group of the block's first row, and
+ * the first row is padding only if the whole block is.  Only rows whose entry equals
+ * their block's group are written; rows with -1 are not.
  * m_total must be a multiple of 128 (DG_ERR_INVALID_ARG otherwise). */
 int dg_m_grouped_gemm_fp8_contiguous(const void* a, const float* sa, long ld_sa,
                                      const void* b, const float* sb,
@@ -160,15 +166,18 @@ enum { DG_DTYPE_F32 = 0, DG_DTYPE_BF16 = 1 };
  * (1 if amax == 0), q = E4M3 RNE of fp32(x / scale), saturating at +-448, NaN -> 0x7F.
  * Requires k % 128 == 0 (DG_ERR_UNSUPPORTED), x 16-byte aligned with ldx a multiple of
  * 16 bytes / element size, q 8-byte aligned with ldq % 8 == 0, ld_sa >= rows (else
- * DG_ERR_MISALIGNED / DG_ERR_INVALID_ARG).  rows == 0 is a no-op.  Asynchronous on
+ * DG_ERR_INVALID_ARG), and sa 16-byte aligned with ld_sa a multiple of 4 -- the sA the
+ * GEMMs accept; dg_get_aligned_ld_sa gives the smallest such ld_sa (else
+ * DG_ERR_MISALIGNED).  Leading dimensions so large that rows * ld * 4 would not fit
+ * in 63 bits give DG_ERR_UNSUPPORTED.  rows == 0 is a no-op.  Asynchronous on
  * `stream`; nothing is allocated. */
 int dg_quantize_fp8_1x128(const void* x, int x_dtype, long ldx, int rows, int k,
                           void* q, long ldq, float* sa, long ld_sa, void* stream);
 
 /* FP8 cast with per-128x128 scales (the B-side granularity).
  *   x  [rows][ldx] fp32 or bf16       q [rows][ldq] E4M3       sb [ceil(rows/128)][k/128]
- * Same rounding and requirements as dg_quantize_fp8_1x128; a ragged last row block
- * takes its amax over the rows it has. */
+ * Same rounding and requirements as dg_quantize_fp8_1x128 (sb needs 4-byte alignment
+ * only); a ragged last row block takes its amax over the rows it has. */
 int dg_quantize_fp8_128x128(const void* x, int x_dtype, long ldx, int rows, int k,
                             void* q, long ldq, float* sb, void* stream);
 
@@ -183,18 +192,34 @@ int dg_quantize_fp8_1x128_fmt(const void* x, int x_dtype, long ldx, int rows, in
 int dg_quantize_fp8_128x128_fmt(const void* x, int x_dtype, long ldx, int rows, int k,
                                 void* q, long ldq, float* sb, int q_fmt, void* stream);
 
-/* Pin the kernel configuration (an id reported by dg_describe_launch) for every
- * later call of that configuration's layout, overriding the planner; -1 restores
- * automatic planning for all layouts.  Meant for tuning and for tests that
- * compare tile shapes.  Unknown ids give DG_ERR_INVALID_ARG.  Process-wide. */
-int dg_set_kernel_config(int config_id);
+/* Leading dimension (in floats) that an MN-major sA of `rows` rows needs: rows rounded
+ * up to a multiple of 4, so that every K block's scales start 16-byte aligned (the
+ * README's utility get_tma_aligned_size, for the GEMMs here).  rows < 0 gives
+ * DG_ERR_INVALID_ARG, rows above LONG_MAX - 3 DG_ERR_UNSUPPORTED.  Host only. */
+long dg_get_aligned_ld_sa(long rows);
 
-/* Enumerate the compiled kernel configurations: for index 0, 1, ... fills
- * out[0..6] = config id, layout, block_m, block_n, waves per workgroup, 1 if
- * the configuration also runs E5M2 operands (the _fmt calls) else 0, and 1 if it
- * has instances compiled for fixed K (see dg_describe_launch) else 0, and
- * returns DG_OK; past the last one returns DG_ERR_INVALID_ARG.  Host only. */
-int dg_kernel_config_info(int index, int* out);
+/* The README's other sA utility (get_col_major_tma_aligned_tensor): turn per-row scales
+ * stored row-major into the MN-major layout the GEMMs read.
+ *   sa_in  [groups][rows][ld_in]    fp32, device; sa_in[(g*rows + r)*ld_in + kb]
+ *   sa_out [groups][kblocks][ld_sa] fp32, device; sa_out[(g*kblocks + kb)*ld_sa + r]
+ * (groups = 1 for the dense and contiguous layouts, G for the masked one.)  Columns
+ * rows .. ld_sa-1 of sa_out are left as they are.  Requires ld_in >= kblocks and
+ * ld_sa >= rows (else DG_ERR_INVALID_ARG), sa_in 4-byte and sa_out 16-byte aligned and
+ * ld_sa % 4 == 0 (else DG_ERR_MISALIGNED), rows * ld_in and kblocks * ld_sa below 2^31
+ * and groups <= 65535 (else DG_ERR_UNSUPPORTED).  The two buffers must not overlap.
+ * rows == 0 or kblocks == 0 is a no-op.  Asynchronous on `stream`. */
+int dg_transform_sa_mn_major(const float* sa_in, long ld_in, float* sa_out, long ld_sa,
+                             int rows, int kblocks, int groups, void* stream);
+
+/* Check, on the host, the precondition the contiguous layout places on m_indices (a
+ * HOST copy of it): m_total a multiple of dg_get_m_alignment(); every entry a group in
+ * [0, num_groups) or -1; in each aligned 128-row block, every entry either -1 or the
+ * group of the block's first row (so a block whose first row is padding is all
+ * padding).  Returns DG_OK, or DG_ERR_INVALID_ARG with *bad_row (if bad_row is not
+ * NULL) set to the first offending row (m_total when m_total is not aligned); bad_row
+ * is -1 on success.  The GEMM itself never reads m_indices on the host: a block that
+ * breaks the rule gets only its first row's group computed and written. */
+int dg_check_contiguous_layout(const int* m_indices, int m_total, int num_groups, int* bad_row);
 
 /* Host-only tile planner, exposed for inspection and tests; it touches no device.
  * Among candidate block shapes (block_ms[i], block_ns[j]) with per-shape relative
@@ -208,17 +233,6 @@ int dg_kernel_config_info(int index, int* out);
 int dg_plan_tiles(int m, int n, int num_units, int blocks_per_unit,
                   const int* block_ms, int n_bm, const int* block_ns, int n_bn,
                   const double* eff, int* out);
-
-/* Describe the kernel configuration a call with these sizes would launch, without
- * launching (layout 0 dense, 1 contiguous, 2 masked).  out[0..7] = block_m,
- * block_n, waves per workgroup, tiles (upper bound for masked), persistent grid
- * size, config id, row tiles per raster group of the tile order (0 for masked,
- * whose order follows the groups), and K/128 if the launch uses an instance
- * compiled for that K (K = 7168 or 2048 in some configurations), else 0; out
- * must hold 8 ints.  num_cus <= 0 uses
- * dg_get_num_cus().  Needs no device if num_cus > 0 and assumes one resident
- * workgroup per CU for the big shapes. */
-int dg_describe_launch(int layout, int m, int n, int k, int num_groups, int num_cus, int* out);
 
 #ifdef __cplusplus
 }

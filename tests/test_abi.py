@@ -10,7 +10,7 @@ import pytest
 import fp8_block_scaled_e4m3_amd as dg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dg.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("dg.h", "dg_tuning.h")]
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -20,9 +20,15 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_header_is_checked():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(os.path.basename(h) for h in HEADERS)
 
 
 def test_header_symbols_exported(lib):
@@ -223,3 +229,60 @@ def test_quantize_validation(lib):
     assert q1f(P(16), 0, 256, 4, 200, P(16), 256, P(16), 4, 1, None) == dg.DG_ERR_UNSUPPORTED
     assert q2f(P(16), 1, 388, 4, 384, P(16), 384, P(16), 1, None) == dg.DG_ERR_MISALIGNED
     assert q1f(P(16), 0, 256, 0, 256, P(16), 256, P(16), 4, 1, None) == dg.DG_OK
+
+
+def test_quantize_1x128_takes_only_an_sa_the_gemm_accepts(lib):
+    P = ctypes.c_void_p
+    q1 = lib.dg_quantize_fp8_1x128
+    assert q1(P(16), 0, 256, 6, 256, P(16), 256, P(16), 6, None) == dg.DG_ERR_MISALIGNED      # ld_sa % 4
+    assert q1(P(16), 0, 256, 6, 256, P(16), 256, P(20), 8, None) == dg.DG_ERR_MISALIGNED      # sa not 16-aligned
+    assert q1(P(16), 0, 256, 6, 256, P(16), 256, P(16), 5, None) == dg.DG_ERR_INVALID_ARG     # ld_sa < rows
+    assert lib.dg_quantize_fp8_1x128_fmt(P(16), 0, 256, 6, 256, P(16), 256, P(16), 6, 1, None) == \
+        dg.DG_ERR_MISALIGNED
+
+
+def test_aligned_ld_sa():
+    assert [dg.dg_get_aligned_ld_sa(r) for r in (0, 1, 3, 4, 5, 4096, 4097)] == [0, 4, 4, 4, 8, 4096, 4100]
+    with pytest.raises(dg.DGError):
+        dg.dg_get_aligned_ld_sa(-1)
+
+
+def test_transform_sa_validation(lib):
+    P = ctypes.c_void_p
+    t = lib.dg_transform_sa_mn_major
+    assert t(P(16), 55, P(16), 4096, 4096, 56, 1, None) == dg.DG_ERR_INVALID_ARG   # ld_in < kblocks
+    assert t(P(16), 56, P(16), 4095, 4096, 56, 1, None) == dg.DG_ERR_INVALID_ARG   # ld_sa < rows
+    assert t(P(16), 56, P(16), 4098, 4097, 56, 1, None) == dg.DG_ERR_MISALIGNED    # ld_sa % 4
+    assert t(P(16), 56, P(24), 4100, 4097, 56, 1, None) == dg.DG_ERR_MISALIGNED    # out not 16-aligned
+    assert t(P(18), 56, P(16), 4100, 4097, 56, 1, None) == dg.DG_ERR_MISALIGNED    # in not 4-aligned
+    assert t(None, 56, P(16), 4100, 4097, 56, 1, None) == dg.DG_ERR_INVALID_ARG
+    assert t(P(16), 56, P(16), 4100, 4097, 56, 0, None) == dg.DG_ERR_INVALID_ARG   # groups < 1
+    assert t(P(16), 56, P(16), 4100, 4097, 56, 70000, None) == dg.DG_ERR_UNSUPPORTED
+    assert t(P(16), 56, P(16), 4100, 0, 56, 1, None) == dg.DG_OK                   # empty: no-op
+    assert t(P(16), 56, P(16), 4100, 4097, 0, 1, None) == dg.DG_OK
+
+
+def test_contiguous_layout_checker():
+    import numpy as np
+
+    def layout(counts, ng):
+        mi = []
+        for g, c in enumerate(counts):
+            p = -(-c // 128) * 128
+            mi += [g] * c + [-1] * (p - c)
+        return np.array(mi, np.int32), ng
+
+    mi, ng = layout([130, 0, 1, 257, 128], 5)
+    assert dg.dg_check_contiguous_layout(mi, ng) is None
+    assert dg.dg_check_contiguous_layout(np.zeros(0, np.int32), 1) is None
+    assert dg.dg_check_contiguous_layout(mi[:200], ng) == 200            # not a multiple of 128
+    bad = mi.copy(); bad[5] = 7                                           # group out of range
+    assert dg.dg_check_contiguous_layout(bad, ng) == 5
+    bad = mi.copy(); bad[3] = -2                                          # not a group, not -1
+    assert dg.dg_check_contiguous_layout(bad, ng) == 3
+    bad = mi.copy(); bad[129] = 3                                         # another group inside a block
+    assert dg.dg_check_contiguous_layout(bad, ng) == 129
+    bad = mi.copy(); bad[384] = -1                                        # block starts with padding ...
+    assert dg.dg_check_contiguous_layout(bad, ng) == 385                  # ... but holds rows of group 3
+    ok = mi.copy(); ok[130:140] = 0; ok[135] = -1                         # padding between rows of the group
+    assert dg.dg_check_contiguous_layout(ok, ng) is None

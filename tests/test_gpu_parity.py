@@ -1,18 +1,18 @@
 """GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
 
-Small and ragged shapes are compared element by element over the whole output;
-the full-size workloads are run in the launch configuration the bench times and
-checked on sampled rows (all columns) against the oracle, plus whole-output
-properties: no NaN/Inf, untouched padding / masked rows bit-exact, grouped output
-equal to the dense kernel's output per group bit for bit.
+Every output is compared element by element with the oracle over all of its valid
+rows: small and ragged shapes on every compiled configuration, and the full-size
+workloads in the launch configuration the bench times.  Whole-output properties
+are checked bit-exactly as well: no NaN/Inf, untouched padding / masked rows,
+nothing written past column N, grouped output equal to the dense kernel's output
+per group.
 """
 import numpy as np
 import pytest
 
 import fp8_block_scaled_e4m3_amd as dg
 import workloads as W
-from tests.gpu_support import (bits, check_values, require_gpu, sample_rows, say, sentinel_like, to_dev,
-                               upload)
+from tests.gpu_support import bits, check_values, require_gpu, say, sentinel_like, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -90,15 +90,14 @@ def test_dense_under_filled_workload_full_compare(orc):
     check_values(out, ref, "dense 256x7168x2048")
 
 
-def test_dense_prefill_workload_sampled(orc):
+def test_dense_prefill_workload_full_compare(orc):
     dd = W.make(W.WORKLOADS["dense_m4096_n7168_k7168"])
     say("dense 4096x7168x7168 (planned config)", dg.dg_describe_launch(0, 4096, 7168, 7168, 1))
     out, full = run_dense(dd)
     assert np.all(full[:, 7168:] == W.SENTINEL_BF16)
     assert not np.any(out == W.SENTINEL_BF16)
-    rows = sample_rows(4096, 256, 48)
-    ref = oracle_dense(orc, dd, rows)
-    check_values(out[rows], ref, "dense 4096x7168x7168 sampled rows")
+    say("dense 4096x7168x7168: oracle over all rows")
+    check_values(out, oracle_dense(orc, dd), "dense 4096x7168x7168 all rows")
 
 
 def test_dense_cu_cap_is_bit_identical(orc):
@@ -228,31 +227,53 @@ def test_contiguous_chained_tiles_all_configs(orc, k):
         dg.dg_set_num_cus(0)
 
 
-def test_contiguous_workload_sampled(orc):
+def test_contiguous_workload_full_compare(orc):
     w = W.WORKLOADS["contiguous_g8_t32768_zipf1.1_n4096_k7168"]
     cd = W.make(w)
     say("contiguous 8x4096x7168 zipf (planned config)",
         dg.dg_describe_launch(1, cd["m_total"], 4096, 7168, 8))
     out = run_contiguous(cd)
     valid = cd["m_indices"] >= 0
-    assert np.all(out[~valid] == W.SENTINEL_BF16)
-    assert not np.any(out[valid] == W.SENTINEL_BF16)
+    assert np.all(out[~valid] == W.SENTINEL_BF16), "a padding row was written"
+    assert not np.any(out[valid] == W.SENTINEL_BF16), "a valid row was not written"
+    say("contiguous 8x4096x7168 zipf: oracle over all valid rows")
+    sentinel = np.full(out.shape, W.SENTINEL_BF16, np.uint16)
+    ref = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], cd["m_indices"], d_init=sentinel)
+    check_values(out[valid], ref[valid], "contiguous workload all valid rows")
+    # grouped == dense per group, bit for bit, on every group
     off = 0
-    rows, groups = [], []
     for g, (c, p) in enumerate(zip(cd["counts"], W.padded(cd["counts"]))):
-        r = off + sample_rows(c, 128, 6, seed=g)
-        rows.extend(r.tolist())
-        groups.extend([g] * len(r))
+        say(f"contiguous workload: group {g} ({c} rows) against the dense kernel")
+        assert np.array_equal(dense_gpu_segment(cd, g, off, off + c), out[off:off + c]), f"group {g}"
         off += p
-    rows = np.array(rows)
-    ref = np.empty((len(rows), 4096), np.uint16)
-    for g in range(8):
-        sel = np.array(groups) == g
-        ref[sel] = orc.gemm_fp8_nt(cd["a"][rows[sel]], cd["sa"][:, rows[sel]], cd["b"][g], cd["sb"][g])
-    check_values(out[rows], ref, "contiguous workload sampled rows")
-    # grouped == dense per group, bit for bit, on the smallest group
-    lo = sum(W.padded(cd["counts"])[:7])
-    assert np.array_equal(dense_gpu_segment(cd, 7, lo, lo + cd["counts"][7]), out[lo:lo + cd["counts"][7]])
+
+
+def test_contiguous_rows_breaking_the_block_rule_are_not_written(orc):
+    """m_indices that break the layout's precondition (an entry naming another group or
+    an out-of-range group inside a 128-row block): the call computes each block for the
+    group of its first row and writes only the rows that carry that group, so the
+    offending rows keep their previous contents; the others are exact."""
+    counts = [200, 130, 60]
+    cd = W.make_contiguous(counts, n=144, k=256, seed=51)
+    mi = cd["m_indices"].copy()
+    mi[5] = 1            # group 0's first block: a row naming group 1
+    mi[140] = 2          # group 0's second block (rows 128..199 valid)
+    mi[300] = 9          # group 1's second block: out of range
+    mi[260] = -1         # padding inside group 1's rows (allowed)
+    assert dg.dg_check_contiguous_layout(mi, 3) == 5
+    cd2 = dict(cd, m_indices=mi)
+    for cfg in configs_of(1):
+        say(f"contiguous with broken blocks cfg={cfg}")
+        out = run_contiguous(cd2, cfg)
+        keep = np.zeros(cd["m_total"], bool)
+        for b in range(0, cd["m_total"], 128):
+            keep[b:b + 128] = mi[b:b + 128] == mi[b]
+        keep &= mi >= 0
+        assert np.all(out[~keep] == W.SENTINEL_BF16), f"cfg{cfg}: a row outside its block's group was written"
+        sentinel = np.full(out.shape, W.SENTINEL_BF16, np.uint16)
+        ref = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], np.where(keep, mi, -1),
+                                       d_init=sentinel)
+        check_values(out[keep], ref[keep], f"contiguous broken blocks cfg{cfg}")
 
 
 # --------------------------------------------------------------------------- masked
@@ -269,17 +290,19 @@ def run_masked(md, cfg=-1, masked_m=None):
     return bits(out)
 
 
-def check_masked(orc, md, out, groups=None):
+def check_masked(orc, md, out):
+    """Rows >= masked_m untouched and every valid row written (bit-exact), every valid
+    row of every group within tolerance of the oracle (one call's valid rows together)."""
     mm = np.clip(md["masked_m"], 0, md["max_m"])
     for g in range(md["groups"]):
         assert np.all(out[g, mm[g]:] == W.SENTINEL_BF16), f"group {g}: a row >= masked_m was written"
         assert not np.any(out[g, :mm[g]] == W.SENTINEL_BF16), f"group {g}: a valid row was not written"
-    for g in (range(md["groups"]) if groups is None else groups):
-        if mm[g] == 0:
-            continue
-        rows = np.arange(mm[g]) if mm[g] <= 64 else sample_rows(int(mm[g]), 16, 24, seed=g)
-        ref = orc.gemm_fp8_nt(md["a"][g][rows], md["sa"][g][:, rows], md["b"][g], md["sb"][g])
-        check_values(out[g][rows], ref, f"masked group {g}")
+    if mm.sum() == 0:
+        return
+    sentinel = np.full(out.shape, W.SENTINEL_BF16, np.uint16)
+    ref = orc.m_grouped_masked(md["a"], md["sa"], md["b"], md["sb"], mm, d_init=sentinel)
+    valid = np.arange(md["max_m"])[None, :] < mm[:, None]
+    check_values(out[valid], ref[valid], "masked, all valid rows")
 
 
 @pytest.mark.parametrize("max_m", [256, 70])
@@ -315,7 +338,7 @@ def test_masked_all_empty_is_noop():
     assert np.all(out == W.SENTINEL_BF16)
 
 
-def test_masked_workload_sampled(orc):
+def test_masked_workload_full_compare(orc):
     md = W.make(W.WORKLOADS["masked_g16_cap256_n4096_k7168"])
     say("masked 16x256x4096x7168 masked_m=", md["masked_m"].tolist(),
         dg.dg_describe_launch(2, 256, 4096, 7168, 16))

@@ -256,3 +256,93 @@ def test_quant_validation_errors():
     q = torch.zeros((4, 256), dtype=torch.uint8, device="cuda:0")
     with pytest.raises(ValueError):
         dg.dg_quantize_fp8_1x128_fmt(x, q, sa, q_fmt="e3m4")
+
+
+def tie_panel(fmt, scale_exps, seed):
+    """128-row panels, one per scale s: every 1x128 block is [FMAX*s, then values p and
+    their fp32 neighbours, p = t*s for the format's values and rounding ties t], so that
+    each 1x128 and each 128x128 block gets the scale s exactly and its quotients land on
+    and beside every rounding decision.  The scales have 18-bit significands and the t
+    at most 5, so every p is exact."""
+    rng = np.random.default_rng(seed)
+    fmax = 448.0 if fmt == "e4m3" else 57344.0
+    ties = []
+    if fmt == "e4m3":
+        for e in range(-9, 9):
+            for m in range(16):
+                for frac in (0.0, 0.5):
+                    ties.append(2.0 ** e * (1 + (m + frac) / 8) if e >= -6 else (m + frac) * 2.0 ** -9)
+    else:
+        for e in range(-17, 16):
+            for m in range(8):
+                for frac in (0.0, 0.5):
+                    ties.append(2.0 ** e * (1 + (m + frac) / 4) if e >= -14 else (m + frac) * 2.0 ** -16)
+    t = np.array(sorted(set(ties)), np.float64)
+    t = t[t <= fmax]
+    t = np.concatenate([t, -t])
+    panels = []
+    for e in scale_exps:
+        s = (1.0 + int(rng.integers(0, 1 << 17)) / 2.0 ** 17) * 2.0 ** e
+        p = t * s
+        p32 = p.astype(np.float32)
+        assert np.all(p32.astype(np.float64) == p)                              # exact products
+        vals = np.stack([p32, np.nextafter(p32, np.float32(-np.inf)), np.nextafter(p32, np.float32(np.inf))], 1)
+        flat = vals.reshape(-1)
+        step = -(-flat.size // 128)                     # the 128 rows together cover every value
+        x = np.empty((128, 4 * 128), np.float32)
+        for r in range(128):
+            row = np.resize(np.roll(flat, -step * r), 4 * 127).reshape(4, 127)
+            x[r] = np.concatenate([np.full((4, 1), np.float32(fmax * s)), row], axis=1).reshape(-1)
+        panels.append(x)
+    return np.concatenate(panels)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quant_tiny_and_boundary_scales_bit_exact(orc, fmt):
+    """Blocks whose scales sit far below the fast path (2^-120, 2^-100, 2^-80: the
+    software path), at its lower edge (2^-65, 2^-64, 2^-63) and in the normal range,
+    each with values on and beside every rounding decision: codes and scales of both
+    casts equal the oracle's bit for bit."""
+    exps = [-120, -100, -80, -65, -64, -63, -40, 0, 30] if fmt == "e4m3" else [-110, -90, -65, -64, -63, 0, 20]
+    x = tie_panel(fmt, exps, seed=17 if fmt == "e4m3" else 18)
+    rows, k = x.shape
+    say(f"quant tiny/boundary scales {fmt}: {rows}x{k}")
+    q, sa = gpu_1x128(to_dev(x), rows, k, fmt)
+    rq, rsa = orc.quantize_rows_1x128(x, fmt)
+    assert np.array_equal(q, rq), f"1x128: {np.sum(q != rq)} codes differ"
+    assert same_bits(sa[:, :rows], rsa)
+    q, sb = gpu_128x128(to_dev(x), rows, k, fmt)
+    rq, rsb = orc.quantize_blocks_128x128(x, fmt)
+    assert np.array_equal(q, rq), f"128x128: {np.sum(q != rq)} codes differ"
+    assert same_bits(sb, rsb)
+
+
+@pytest.mark.parametrize("rows,kb,groups", [(1, 1, 1), (37, 5, 1), (300, 56, 1), (4097, 16, 1), (70, 9, 3)])
+def test_transform_sa_mn_major(rows, kb, groups):
+    """Row-major per-row scales to the GEMMs' MN-major layout with an aligned leading
+    dimension: a plain transpose, bit for bit; padding columns untouched."""
+    import torch
+    rng = np.random.default_rng(rows + kb)
+    src = rng.standard_normal((groups, rows, kb + 3)).astype(np.float32)   # ld_in = kb + 3
+    x = to_dev(src)[:, :, :kb]
+    ld = dg.dg_get_aligned_ld_sa(rows)
+    out = torch.full((groups, kb, ld), 7.0, device="cuda:0")
+    say(f"transform sa rows={rows} kb={kb} groups={groups}")
+    dg.dg_transform_sa_mn_major(x if groups > 1 else x[0], out if groups > 1 else out[0])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert same_bits(got[:, :, :rows], np.ascontiguousarray(src[:, :, :kb].transpose(0, 2, 1)))
+    assert np.all(got[:, :, rows:] == 7.0)
+
+
+def test_transformed_sa_feeds_the_gemm(orc):
+    """The cast's row-major scales (as the pages' callers hold them) transformed on the GPU
+    and used by the dense GEMM give the oracle's result."""
+    import torch
+    dd = W.make_dense(200, 256, 512, seed=61)
+    rowmajor = to_dev(np.ascontiguousarray(dd["sa"][:, :200].T))           # [rows, K/128]
+    sa = dg.dg_transform_sa_mn_major(rowmajor)
+    d = sentinel_like((200, 256))
+    dg.dg_gemm_fp8_nt(to_dev(dd["a"]), sa, to_dev(dd["b"]), to_dev(dd["sb"]), d)
+    torch.cuda.synchronize()
+    check_values(bits(d), orc.gemm_fp8_nt(dd["a"], dd["sa"], dd["b"], dd["sb"]), "transformed sa + gemm")
