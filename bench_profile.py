@@ -273,7 +273,9 @@ def summarize(args) -> int:
         lines.append(f"mean duration, timed window (last {len(win)} dispatches): {mean(win) / 1e3:.2f} us "
                      f"(min {min(win) / 1e3:.2f}, max {max(win) / 1e3:.2f})" if win else "timed window: none")
         if bench_us is not None:
-            lines.append(f"bench line, same run (HIP events around each timed launch): {bench_us:.2f} us")
+            lines.append(f"bench line of the traced run (one HIP event pair over its timed launches): {bench_us:.2f} us")
+            lines.append("  (the trace adds a few us of dispatch overhead between launches, which the bench line "
+                         "counts and the kernel durations do not: it matters only for kernels of a few tens of us)")
         c = counters.get(key, {})
         if c:
             lines.append("")
