@@ -125,21 +125,36 @@ def input_sets(dv: dict, set_bytes: int, cold: bool) -> list:
     return [dv] + [{k: v.clone() for k, v in dv.items()} for _ in range(n - 1)]
 
 
-def run_timed(calls: list, warmup: int, steps: int):
+def run_timed(calls: list, warmup: int, steps: int, graph: bool = False):
     """`warmup` untimed launches, then `steps` launches back to back between one pair of
     HIP events recorded on the launch stream (no event between launches: event records
     there would idle the GPU for ~10 us each).  Launch i runs calls[i % len(calls)].
+    graph=True captures the timed launches into one HIP graph first and times its
+    replay: a kernel of ~10 us finishes faster than Python can issue the next call, so
+    eagerly issued launches would time the host, not the GPU.
     Returns (mean seconds per launch from the events, wall seconds of the timed steps)."""
     import torch
-    stream = torch.cuda.current_stream()
     for i in range(warmup):
         calls[i % len(calls)]()
+    g = None
+    if graph:
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps):
+                calls[(warmup + i) % len(calls)]()
+    stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for i in range(steps):
-        calls[(warmup + i) % len(calls)]()
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(steps):
+            calls[(warmup + i) % len(calls)]()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -210,10 +225,11 @@ def time_casts(warmup, iters):
             calls = [lambda x=x: dg.dg_quantize_fp8_128x128(x, q, s_) for x in xs]
             nsc = ceil_div(rows, 128) * (k // 128)
         b3 = rows * k * 4 + rows * k + 4 * nsc
-        mean_s, _ = run_timed(calls, warmup, iters)
+        mean_s, _ = run_timed(calls, warmup, iters, graph=True)
         out[cname] = {"us": round(mean_s * 1e6, 2), "gbps": round(b3 / mean_s / 1e9, 1),
                       "frac_hbm": round(b3 / mean_s / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm",
                       "cold_caches": True, "input_copies": len(xs), "warmup": warmup, "steps": iters,
+                      "launch": "hip graph replay",
                       "algorithmic_bytes": b3, "traffic": traffic_for(cname)}
         del x0, xs, q, s_, calls
         torch.cuda.empty_cache()
@@ -319,8 +335,9 @@ def main():
 
     if not args.no_secondary:
         # The other workloads, each after the same number of untimed launches as the
-        # headline; HBM-bound ones cycle through input copies so that every timed launch
-        # reads from HBM (cold L2 and Infinity Cache), MFMA-bound ones reuse one set.
+        # headline, timed as one HIP graph replay of their timed launches; HBM-bound ones
+        # cycle through input copies so that every timed launch reads from HBM (cold L2
+        # and Infinity Cache), MFMA-bound ones reuse one set.
         sec = {}
         for name, ww in W.WORKLOADS.items():
             if name == w.name or name.startswith("dense_m128"):
@@ -333,13 +350,14 @@ def main():
             hbm_bound = f2 / b2 < PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
             sets = input_sets(v2, b2, hbm_bound)
             calls = [make_call(ww, v, o2) for v in sets]
-            mean_s, _ = run_timed(calls, args.warmup, args.secondary_iters)
+            mean_s, _ = run_timed(calls, args.warmup, args.secondary_iters, graph=True)
             sec[name] = {"us": round(mean_s * 1e6, 2), "tflops": round(f2 / mean_s / 1e12, 2),
                          "gbps": round(b2 / mean_s / 1e9, 1),
                          "frac_mfma": round(f2 / mean_s / 1e12 / PEAK_FP8_TFLOPS, 4),
                          "frac_hbm": round(b2 / mean_s / 1e9 / PEAK_HBM_GBS, 4),
                          "bound": "hbm" if hbm_bound else "mfma", "cold_caches": hbm_bound,
                          "input_copies": len(sets), "warmup": args.warmup, "steps": args.secondary_iters,
+                         "launch": "hip graph replay",
                          "algorithmic_flops": f2, "algorithmic_bytes": b2,
                          "traffic": traffic_for(name)}
             if ww.kind == "masked":
@@ -350,7 +368,7 @@ def main():
                 for cap in CU_CAPS:
                     dg.dg_set_num_cus(cap)
                     try:
-                        cs, _ = run_timed(calls, args.warmup, args.secondary_iters)
+                        cs, _ = run_timed(calls, args.warmup, args.secondary_iters, graph=True)
                     finally:
                         dg.dg_set_num_cus(0)
                     capped[str(cap)] = {"us": round(cs * 1e6, 2), "gbps": round(b2 / cs / 1e9, 1)}
