@@ -377,11 +377,11 @@ def dg_set_kernel_config(config_id: int) -> None:
 
 def dg_kernel_config_info() -> list:
     """All compiled kernel configurations as dicts (id, layout, block_m, block_n, waves,
-    all_formats: whether E5M2 operands run in it, k_specialised: whether it has
-    instances compiled for fixed K)."""
+    all_formats: whether E5M2 operands run in it, shape_specialised: whether it has
+    instances compiled for fixed N and K)."""
     out, res, i = (ctypes.c_int * 7)(), [], 0
     while load_library().dg_kernel_config_info(i, out) == DG_OK:
-        res.append(dict(zip(("id", "layout", "block_m", "block_n", "waves", "all_formats", "k_specialised"),
+        res.append(dict(zip(("id", "layout", "block_m", "block_n", "waves", "all_formats", "shape_specialised"),
                             list(out))))
         i += 1
     return res

@@ -104,12 +104,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_fmt(int f) { return f == DG_FMT_E4M3 || f == DG_FMT_E5M2; }
 
-// K/128 of the compile-time-K instance a launch of config c uses, 0 for the generic one
-// (the selection made by the config's launcher: K/128 in kSpecKBlocks, any operand format)
+// K/128 of the shape instance (N and K fixed at compile time) a launch of config c
+// uses, 0 for the generic one (the selection the config's launcher makes: the call's N
+// and K/128 listed in kSpecShapes for the config's layout, any operand format)
 int specialised_kblocks(const KernelConfig& c, const GemmParams& p) {
-    if (!c.k_specialised) return 0;
-    for (int kb : dg::kSpecKBlocks)
-        if (p.kblocks == kb) return kb;
+    if (!c.shape_specialised) return 0;
+    for (const dg::SpecShape& s : dg::kSpecShapes)
+        if (s.grouped == (c.layout != dg::kDense) && s.n == p.n && s.kblocks == p.kblocks) return s.kblocks;
     return 0;
 }
 
@@ -414,7 +415,7 @@ int dg_kernel_config_info(int index, int* out) {
     out[3] = cfgs[index].bn;
     out[4] = cfgs[index].wm * cfgs[index].wn;
     out[5] = cfgs[index].all_formats ? 1 : 0;
-    out[6] = cfgs[index].k_specialised ? 1 : 0;
+    out[6] = cfgs[index].shape_specialised ? 1 : 0;
     return DG_OK;
 }
 

@@ -93,9 +93,10 @@ __device__ __forceinline__ void wait_vmem_le() {
 // the accumulator arrays it captures by reference into scratch memory.
 #define DG_INLINE __attribute__((always_inline))
 
-// f(integral_constant<I>) for I = B .. E-1, unrolled at compile time.
+// f(integral_constant<I>) for I = B .. E-1, unrolled at compile time (kernels and the
+// host-side instance selection).
 template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
+__host__ __device__ __forceinline__ void static_for(F&& f) {
     if constexpr (B < E) {
         f(std::integral_constant<int, B>{});
         static_for<B + 1, E>(f);
@@ -115,9 +116,10 @@ __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC0
 // FMT: operand formats, bit 0 = A is E5M2, bit 1 = B is E5M2 (else E4M3).  The
 // matrix instruction's format fields take them directly (B rows feed the
 // instruction's first operand, A rows its second).
-// KC > 0: an instance for K/128 == KC only (loop trip counts and the split into
-// stage groups are then compile-time constants); 0: any K.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int KC>
+// NC, KC > 0: an instance for N == NC and K/128 == KC only (tile counts, scale-row
+// offsets, the column guard, loop trip counts and the split into stage groups are
+// then compile-time constants); 0: any N, K.
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int NC, int KC>
 __global__ void __launch_bounds__(WM * WN * 64)
 dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const float* __restrict__ sa_ptr,
                const uint8_t* __restrict__ b_ptr, const float* __restrict__ sb_ptr, uint16_t* __restrict__ d_ptr) {
@@ -162,6 +164,11 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     const int lsub = lane & (MF - 1);             // row of the sub-tile this lane feeds / owns
     const int lgrp = lane / MF;                   // K group of the lane inside an operand fragment
     const int KB = KC > 0 ? KC : p.kblocks;
+    static_assert((NC > 0) == (KC > 0), "shape instances fix N and K together");
+    const int NN = NC > 0 ? NC : p.n;
+    const int TILES_N = NC > 0 ? (NC + BN - 1) / BN : p.tiles_n;
+    const int NBLK = NC > 0 ? (NC + kKBlock - 1) / kKBlock : p.nblocks;
+    constexpr bool WHOLE_N = NC > 0 && NC % BN == 0;   // no tile has columns past N
 
     // ---- masked layout: valid row blocks per group, exclusive prefix in LDS ----
     int total_tiles = p.num_tiles;
@@ -196,7 +203,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
             if (lane == 63) s_prefix[G] = incl;
         }
         __syncthreads();
-        total_tiles = s_prefix[G] * p.tiles_n;
+        total_tiles = s_prefix[G] * TILES_N;
     }
 
     const int P = gridDim.x;
@@ -275,7 +282,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 // group g owns tiles [prefix[g], prefix[g+1]) * tiles_n, ordered N block
                 // major and row block minor, so the row blocks sharing one B tile are
                 // neighbours in the hand-out (same XCD, same step: B comes from L2 once)
-                const int q = L / p.tiles_n;
+                const int q = L / TILES_N;
                 int lo = 0, hi = p.num_groups;           // largest g with prefix[g] <= q
                 while (hi - lo > 1) {
                     const int mid = (lo + hi) >> 1;
@@ -283,14 +290,14 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                 }
                 g = lo;
                 const int vb = s_prefix[g + 1] - s_prefix[g];
-                const int t = L - s_prefix[g] * p.tiles_n;
+                const int t = L - s_prefix[g] * TILES_N;
                 nb = t / vb;
                 mb = t - nb * vb;
                 int mm = p.masked_m[g];
                 mm = mm < 0 ? 0 : (mm > p.rows ? p.rows : mm);
                 valid_rows = mm - mb * BM;
             } else {
-                const int gsz = p.group_m * p.tiles_n;
+                const int gsz = p.group_m * TILES_N;
                 const int grp = L / gsz;
                 const int first_m = grp * p.group_m;
                 const int gm = min(p.tiles_m - first_m, p.group_m);
@@ -363,7 +370,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         // copies return zeros without a memory access (their outputs are never stored).
         const int a_rows_read = LAYOUT == kMasked ? valid_rows : p.rows - m0;
         t.rs_a = make_rsrc(a_tile, (long)a_rows_read * p.lda);
-        t.rs_b = make_rsrc(b_tile, (long)(p.n - n0) * p.ldb);
+        t.rs_b = make_rsrc(b_tile, (long)(NN - n0) * p.ldb);
         t.rs_sa = make_rsrc(sa_tile, ((long)KB * p.ld_sa - m0) * 4);
         // Sub-tile column fn (MF columns, inside one 128-column scale block because MF
         // divides 128 and the column offsets are multiples of MF) reads its B scales
@@ -373,10 +380,10 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         t.wcol0 = n0 + wn * WTN;
         t.hi_mask = 0;
         if constexpr (MF == 16) {
-            const int nb_lo = min(t.wcol0 / kKBlock, p.nblocks - 1);
+            const int nb_lo = min(t.wcol0 / kKBlock, NBLK - 1);
             t.sb_off[0] = nb_lo * KB * 4;
             if constexpr (!ONE_SB) {
-                t.sb_off[NSB - 1] = min(nb_lo + 1, p.nblocks - 1) * KB * 4;
+                t.sb_off[NSB - 1] = min(nb_lo + 1, NBLK - 1) * KB * 4;
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
                     if ((t.wcol0 + fn * MF) / kKBlock > nb_lo) t.hi_mask |= 1u << fn;
@@ -384,7 +391,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         } else {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                t.sb_off[fn] = min((t.wcol0 + fn * MF) / kKBlock, p.nblocks - 1) * KB * 4;
+                t.sb_off[fn] = min((t.wcol0 + fn * MF) / kKBlock, NBLK - 1) * KB * 4;
         }
         t.active = wm * WTM < t.row_hi && wm * WTM + WTM > t.row_lo;
     };
@@ -842,12 +849,12 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
                                                                          false);
                         // lane group g now holds sub-tile fn + (g & 1), columns 8*(g >> 1) .. +7
                         const int col = cur.wcol0 + (fn + (lgrp & 1)) * MF + (lgrp >> 1) * 8;
-                        if (row_ok && col < p.n) *(uint4*)(drow + col) = uint4{s0[0], s1[0], s0[1], s1[1]};
+                        if (row_ok && (WHOLE_N || col < NN)) *(uint4*)(drow + col) = uint4{s0[0], s1[0], s0[1], s1[1]};
                     }
                     if constexpr (FN % 2 == 1) {
                         const vacc& x = acc[fm][FN - 1];
                         const int col = cur.wcol0 + (FN - 1) * MF + lgrp * 4;
-                        if (row_ok && col < p.n) *(uint2*)(drow + col) = uint2{pack2(x[0], x[1]), pack2(x[2], x[3])};
+                        if (row_ok && (WHOLE_N || col < NN)) *(uint2*)(drow + col) = uint2{pack2(x[0], x[1]), pack2(x[2], x[3])};
                     }
                 } else {
 #pragma unroll
@@ -855,7 +862,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
 #pragma unroll
                         for (int q = 0; q < NACC / 4; ++q) {
                             const int col = cur.wcol0 + fn * MF + q * 8 + lgrp * 4;
-                            if (row_ok && col < p.n)
+                            if (row_ok && (WHOLE_N || col < NN))
                                 *(uint2*)(drow + col) = uint2{pack2(acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1]),
                                                               pack2(acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3])};
                         }
@@ -891,26 +898,34 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     if constexpr (PIPE) wait_vmem_le<0>();
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int KC = 0>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int NC = 0, int KC = 0>
 static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE, FMT, KC>), dim3(grid),
+    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE, FMT, NC, KC>), dim3(grid),
                        dim3(WM * WN * 64), 0, s, p, p.a, p.sa, p.b, p.sb, p.d);
     return hipGetLastError();
 }
 
-// The instance for operand formats FMT: compiled for K/128 == kSpecKBlocks[i] when the
-// configuration has such instances (KSPEC) and the call's K matches; pipelined (the
-// next tile's first NST blocks run as the tail of the current one) when K/128 splits
-// into whole groups of NST and the configuration fits that variant's registers
-// (PIPE_OK); else the generic per-tile loop.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool KSPEC, int FMT>
+// The instance for operand formats FMT: the one compiled for the call's N and K when
+// the configuration has shape instances (SPEC) and kSpecShapes lists them for its
+// layout; pipelined (the next tile's first NST blocks run as the tail of the current
+// one) when K/128 splits into whole groups of NST and the configuration fits that
+// variant's registers (PIPE_OK); else the generic per-tile loop.
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool SPEC, int FMT>
 static hipError_t launch_fmt(const GemmParams& p, int grid, hipStream_t s) {
-    static_assert(sizeof(kSpecKBlocks) / sizeof(kSpecKBlocks[0]) == 2, "one branch per specialised K");
-    if constexpr (KSPEC) {
-        constexpr int K0 = kSpecKBlocks[0], K1 = kSpecKBlocks[1];
-        constexpr bool P0 = PIPE_OK && K0 % NST == 0, P1 = PIPE_OK && K1 % NST == 0;
-        if (p.kblocks == K0) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, P0, FMT, K0>(p, grid, s);
-        if (p.kblocks == K1) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, P1, FMT, K1>(p, grid, s);
+    if constexpr (SPEC) {
+        bool done = false;
+        hipError_t e = hipSuccess;
+        static_for<0, kNumSpecShapes>([&](auto i) {
+            constexpr SpecShape sh = kSpecShapes[decltype(i)::value];
+            if constexpr (sh.grouped == (LAYOUT != kDense)) {
+                constexpr bool PIPE = PIPE_OK && sh.kblocks % NST == 0;
+                if (!done && p.n == sh.n && p.kblocks == sh.kblocks) {
+                    e = launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE, FMT, sh.n, sh.kblocks>(p, grid, s);
+                    done = true;
+                }
+            }
+        });
+        if (done) return e;
     }
     if constexpr (PIPE_OK) {
         if (p.kblocks % NST == 0) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, true, FMT>(p, grid, s);
@@ -920,25 +935,25 @@ static hipError_t launch_fmt(const GemmParams& p, int grid, hipStream_t s) {
 
 // Configurations with ALL_FMT have instances for the four operand-format pairs (E5M2 on
 // either side); the planner gives the others E4M3 operands only.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool ALL_FMT, bool KSPEC>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool ALL_FMT, bool SPEC>
 static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
     if constexpr (ALL_FMT) {
         switch (p.fmt) {
-            case 1: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, KSPEC, 1>(p, grid, s);
-            case 2: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, KSPEC, 2>(p, grid, s);
-            case 3: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, KSPEC, 3>(p, grid, s);
+            case 1: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 1>(p, grid, s);
+            case 2: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 2>(p, grid, s);
+            case 3: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 3>(p, grid, s);
             default: break;
         }
     }
     if (p.fmt != 0) return hipErrorInvalidValue;
-    return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, KSPEC, 0>(p, grid, s);
+    return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 0>(p, grid, s);
 }
 
 template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK>
 static hipError_t occupancy_cfg(int* blocks) {
     typedef void (*KernelFn)(const GemmParams, const uint8_t*, const float*, const uint8_t*, const float*, uint16_t*);
-    const KernelFn k0 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, false, 0, 0>;
-    const KernelFn k1 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, 0, 0>;
+    const KernelFn k0 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, false, 0, 0, 0>;
+    const KernelFn k1 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, 0, 0, 0>;
     int b0 = 0, b1 = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, reinterpret_cast<const void*>(k0), WM * WN * 64, 0);
     if (e == hipSuccess)
@@ -947,9 +962,9 @@ static hipError_t occupancy_cfg(int* blocks) {
     return e;
 }
 
-#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF, PIPE_OK, ALL_FMT, KSPEC)                              \
-    {ID, LAYOUT, BM, BN, WM, WN, EFF, ALL_FMT, KSPEC,                                                           \
-     &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, ALL_FMT, KSPEC>,                                     \
+#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF, PIPE_OK, ALL_FMT, SPEC)                               \
+    {ID, LAYOUT, BM, BN, WM, WN, EFF, ALL_FMT, SPEC,                                                            \
+     &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, ALL_FMT, SPEC>,                                      \
      &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>},
 
 static const KernelConfig kConfigs[] = {DG_CONFIG_TABLE(DG_CFG)};

@@ -34,19 +34,26 @@ struct KernelConfig {
     int bm, bn, wm, wn;
     double eff;            // relative throughput used by the planner
     bool all_formats;      // compiled for E5M2 operands too (else E4M3 only)
-    bool k_specialised;    // has instances with K/128 fixed at compile time (kSpecKBlocks)
+    bool shape_specialised;   // has instances for the shapes of kSpecShapes (N and K fixed at compile time)
     hipError_t (*launch)(const GemmParams&, int grid, hipStream_t);
     hipError_t (*occupancy)(int* blocks_per_cu);
 };
 
-// K/128 values with their own compiled instances (every operand format the configuration
-// runs) in the configurations marked k_specialised: K = 7168 and K = 2048, the hidden and expert widths of the
-// DeepSeek-V3 shapes the workloads use.
-constexpr int kSpecKBlocks[2] = {56, 16};
+// Shapes with their own compiled instances in the configurations marked
+// shape_specialised (N and K/128 are compile-time constants there; every operand
+// format the configuration runs):
+// the DeepSeek-V3 projections of the workloads -- dense N = 7168 with K = 7168 (hidden
+// width) or K = 2048 (expert width), grouped (contiguous and masked) N = 4096, K = 7168.
+struct SpecShape {
+    bool grouped;          // contiguous and masked layouts (else dense)
+    int n, kblocks;
+};
+constexpr SpecShape kSpecShapes[] = {{false, 7168, 56}, {false, 7168, 16}, {true, 4096, 56}};
+constexpr int kNumSpecShapes = sizeof(kSpecShapes) / sizeof(kSpecShapes[0]);
 
 // The compiled tile configurations: X(id, layout, BLOCK_M, BLOCK_N, waves along M, waves
 // along N, MFMA tile (16 or 32), LDS stages, relative throughput for the planner,
-// pipelined variant fits the registers, E5M2 instances, compile-time-K instances).
+// pipelined variant fits the registers, E5M2 instances, shape instances).
 // dg_gemm.hip instantiates a kernel for each row; the planner reads the same rows.
 #define DG_CONFIG_TABLE(X)                                                   \
     /* dense */                                                              \
@@ -60,13 +67,13 @@ constexpr int kSpecKBlocks[2] = {56, 16};
     X(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false, false, false)    \
     X(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false, true, false)     \
     X(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95, true, false, false)     \
-    X(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false, true, false)     \
+    X(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false, true, true)      \
     /* masked */                                                             \
     X(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false, false, false)        \
     X(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false, true, false)         \
     X(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false, false, false)        \
     X(23, kMasked, 128, 256, 2, 4, 16, 3, 0.90, false, false, false)        \
-    X(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, true, false)
+    X(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, true, true)
 
 // Table of compiled configurations (defined in dg_gemm.hip).
 const KernelConfig* kernel_configs(int* count);

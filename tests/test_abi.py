@@ -194,18 +194,25 @@ def test_describe_launch_shapes():
     assert (d["block_m"], d["block_n"], d["grid"]) == (256, 128, 224)
 
 
-def test_describe_reports_k_specialised_instances():
-    """The dense shapes with K = 7168 and K = 2048 run instances compiled for that K;
-    other K, and configurations without such instances, run the generic kernel."""
-    specs = {c["id"] for c in dg.dg_kernel_config_info() if c["k_specialised"]}
-    assert specs and all(c["layout"] == 0 for c in dg.dg_kernel_config_info() if c["k_specialised"])
+def test_describe_reports_shape_instances():
+    """The V3 shapes run instances compiled for their N and K: dense N = 7168 with
+    K = 7168 or 2048, contiguous and masked N = 4096 with K = 7168; another N or K, and
+    configurations without such instances, run the generic kernel."""
+    info = dg.dg_kernel_config_info()
+    specs = {c["id"] for c in info if c["shape_specialised"]}
+    assert {c["layout"] for c in info if c["shape_specialised"]} == {0, 1, 2}
     d = dg.dg_describe_launch(0, 4096, 7168, 7168, 1, 256)
     assert d["config_id"] in specs and d["k_blocks_specialised"] == 56
     d = dg.dg_describe_launch(0, 256, 7168, 2048, 1, 256)
     assert d["config_id"] in specs and d["k_blocks_specialised"] == 16
+    d = dg.dg_describe_launch(1, 33280, 4096, 7168, 8, 256)
+    assert d["config_id"] in specs and d["k_blocks_specialised"] == 56
+    d = dg.dg_describe_launch(2, 256, 4096, 7168, 16, 256)
+    assert d["config_id"] in specs and d["k_blocks_specialised"] == 56
     assert dg.dg_describe_launch(0, 4096, 7168, 4096, 1, 256)["k_blocks_specialised"] == 0
-    assert dg.dg_describe_launch(1, 33280, 4096, 7168, 8, 256)["k_blocks_specialised"] == 0
-    assert dg.dg_describe_launch(2, 256, 4096, 7168, 16, 256)["k_blocks_specialised"] == 0
+    assert dg.dg_describe_launch(0, 4096, 4096, 7168, 1, 256)["k_blocks_specialised"] == 0
+    assert dg.dg_describe_launch(1, 33280, 7168, 2048, 8, 256)["k_blocks_specialised"] == 0
+    assert dg.dg_describe_launch(2, 256, 4096, 2048, 16, 256)["k_blocks_specialised"] == 0
 
 
 def test_quantize_validation(lib):

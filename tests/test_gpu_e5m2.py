@@ -100,15 +100,15 @@ def test_e5m2_large_sampled(orc):
 
 
 @pytest.mark.parametrize("k", [7168, 2048])
-def test_e5m2_k_specialised_instances(orc, k):
-    """At K = 7168 and K = 2048 the E5M2 calls run the instances compiled for that K
-    (pipelined where the K blocks split into stage groups): equal to the oracle, and
-    equal across the configurations carrying them, with one tile per workgroup and
-    with tiles chained on three workgroups."""
-    dd = W.make_dense(300, 464, k, seed=k + 17, a_fmt="e5m2", b_fmt="e4m3")
+def test_e5m2_shape_instances(orc, k):
+    """At N = 7168 with K = 7168 and K = 2048 the E5M2 calls run the instances compiled
+    for that shape (pipelined where the K blocks split into stage groups): equal to the
+    oracle, and equal across the configurations carrying them, with one tile per
+    workgroup and with tiles chained on three workgroups."""
+    dd = W.make_dense(300, 7168, k, seed=k + 17, a_fmt="e5m2", b_fmt="e4m3")
     ref = oracle_fmt(orc, dd)
     specs = [c["id"] for c in dg.dg_kernel_config_info()
-             if c["layout"] == 0 and c["k_specialised"] and c["all_formats"]]
+             if c["layout"] == 0 and c["shape_specialised"] and c["all_formats"]]
     assert specs
     outs = []
     try:

@@ -131,25 +131,26 @@ def test_dense_chained_tiles_all_configs(orc, k):
 
 
 @pytest.mark.parametrize("k", [7168, 2048])
-def test_dense_k_specialised_instances(orc, k):
-    """K = 7168 and K = 2048 run instances compiled for that K in the configurations
-    that have them: their output equals the generic configurations' bit for bit and
-    the oracle, on one tile per workgroup and on three workgroups chaining tiles."""
-    dd = W.make_dense(300, 464, k, seed=k + 9)
+def test_dense_shape_instances(orc, k):
+    """N = 7168 with K = 7168 or K = 2048 runs the instances compiled for that shape in
+    the configurations that have them: their output equals the generic
+    configurations' bit for bit and the oracle, on one tile per workgroup and on three
+    workgroups chaining tiles."""
+    dd = W.make_dense(300, 7168, k, seed=k + 9)
     ref = oracle_dense(orc, dd)
-    specs = [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and c["k_specialised"]]
-    generic = [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and not c["k_specialised"]]
+    specs = [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and c["shape_specialised"]]
+    generic = [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and not c["shape_specialised"]]
     assert specs and generic
     base, _ = run_dense(dd, generic[0])
-    check_values(base, ref, f"dense 300x464x{k} generic cfg{generic[0]}")
+    check_values(base, ref, f"dense 300x7168x{k} generic cfg{generic[0]}")
     try:
         for cap in (0, 3):
             dg.dg_set_num_cus(cap)
             for cfg in specs:
-                say(f"dense 300x464x{k} cfg={cfg} (K-specialised) cu cap {cap}")
+                say(f"dense 300x7168x{k} cfg={cfg} (shape instance) cu cap {cap}")
                 out, full = run_dense(dd, cfg)
                 assert np.array_equal(out, base), f"cfg{cfg} cap {cap} differs from the generic kernel"
-                assert np.all(full[:, 464:] == W.SENTINEL_BF16)
+                assert np.all(full[:, 7168:] == W.SENTINEL_BF16)
     finally:
         dg.dg_set_num_cus(0)
 
@@ -248,6 +249,33 @@ def test_contiguous_workload_full_compare(orc):
         off += p
 
 
+def test_contiguous_shape_instance_all_configs(orc):
+    """N = 4096 with K = 7168 runs the instance compiled for that shape in the contiguous
+    configurations that have one: every contiguous configuration gives the same bits,
+    within tolerance of the oracle, with one tile per workgroup and with three
+    workgroups chaining tiles (two-group tiles and padding included)."""
+    counts = [130, 0, 257, 40]
+    cd = W.make_contiguous(counts, n=4096, k=7168, seed=61)
+    assert any(c["shape_specialised"] for c in dg.dg_kernel_config_info() if c["layout"] == 1)
+    sentinel = np.full((cd["m_total"], 4096), W.SENTINEL_BF16, np.uint16)
+    ref = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], cd["m_indices"], d_init=sentinel)
+    valid = cd["m_indices"] >= 0
+    outs = []
+    try:
+        for cap in (0, 3):
+            dg.dg_set_num_cus(cap)
+            for cfg in configs_of(1):
+                say(f"contiguous counts={counts} n=4096 k=7168 cfg={cfg} cu cap {cap}")
+                out = run_contiguous(cd, cfg)
+                assert np.all(out[~valid] == W.SENTINEL_BF16), "a padding row was written"
+                outs.append(out)
+    finally:
+        dg.dg_set_num_cus(0)
+    check_values(outs[0][valid], ref[valid], "contiguous n=4096 k=7168")
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
 def test_contiguous_rows_breaking_the_block_rule_are_not_written(orc):
     """m_indices that break the layout's precondition (an entry naming another group or
     an out-of-range group inside a 128-row block): the call computes each block for the
@@ -322,6 +350,28 @@ def test_masked_edges_all_configs(orc, max_m):
         seg["sa"] = np.pad(seg["sa"], ((0, 0), (0, (-mm[g]) % 4)))
         dense, _ = run_dense(seg)
         assert np.array_equal(dense, outs[0][g, :mm[g]])
+
+
+def test_masked_shape_instance_all_configs(orc):
+    """N = 4096 with K = 7168 runs the instance compiled for that shape in the masked
+    configurations that have one: every masked configuration gives the same bits,
+    within tolerance of the oracle, with one tile per workgroup and with three
+    workgroups chaining tiles."""
+    mm = [0, 256, 77, 129]
+    md = W.make_masked(len(mm), 256, 4096, 7168, seed=62, masked_m=mm)
+    assert any(c["shape_specialised"] for c in dg.dg_kernel_config_info() if c["layout"] == 2)
+    outs = []
+    try:
+        for cap in (0, 3):
+            dg.dg_set_num_cus(cap)
+            for cfg in configs_of(2):
+                say(f"masked counts={mm} n=4096 k=7168 cfg={cfg} cu cap {cap}")
+                outs.append(run_masked(md, cfg))
+    finally:
+        dg.dg_set_num_cus(0)
+    check_masked(orc, md, outs[0])
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
 
 
 def test_masked_out_of_range_counts_are_clamped(orc):
