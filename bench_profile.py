@@ -134,10 +134,20 @@ def col(row: dict, *names):
     return None
 
 
+def total_size(row: dict, base: str) -> int:
+    """Work-items of a dispatch's grid or workgroup: the kernel trace gives one column
+    per dimension, the counter collection the product."""
+    dims = [col(row, f"{base}_{d}") for d in "XYZ"]
+    if dims[0] is not None:
+        n = 1
+        for d in dims:
+            n *= int(float(d or 1))
+        return n
+    return int(float(col(row, base, base + "s") or 0))
+
+
 def group_key(row: dict) -> tuple:
-    grid = col(row, "Grid_Size_X", "Grid_Size", "Grid_Sizes")
-    wg = col(row, "Workgroup_Size_X", "Workgroup_Size", "Workgroup_Sizes")
-    return (col(row, "Kernel_Name"), int(float(grid or 0)), int(float(wg or 0)))
+    return (col(row, "Kernel_Name"), total_size(row, "Grid_Size"), total_size(row, "Workgroup_Size"))
 
 
 def short_name(kernel: str) -> str:
@@ -301,8 +311,9 @@ def summarize(args) -> int:
                 # GRBM_GUI_ACTIVE is summed over the 8 XCDs; the duration is the same
                 # dispatch's, from the counter run.  For kernels of a few tens of us the
                 # counter window is wider than the kernel and this overstates the clock.
+                note = "" if dur >= 100e3 else " (upper bound: the counter window is wider than this short kernel)"
                 derived.append(("clock (GRBM_GUI_ACTIVE / 8 / duration of the same dispatch)",
-                                f"{gui / 8 / dur:.3f} GHz"))
+                                f"{gui / 8 / dur:.3f} GHz{note}"))
                 derived.append(("mean duration in the counter run", f"{dur / 1e3:.2f} us"))
             mf = cmean("sq_core", "SQ_VALU_MFMA_BUSY_CYCLES")
             if mf is not None and gui:
