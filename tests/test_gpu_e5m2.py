@@ -236,6 +236,45 @@ def test_e5m2_masked(orc, a_fmt, b_fmt):
         assert np.array_equal(o, outs[0])
 
 
+@pytest.mark.parametrize("layout,a_fmt,b_fmt", [(1, "e5m2", "e4m3"), (2, "e4m3", "e5m2")])
+def test_e5m2_grouped_shape_instances(orc, layout, a_fmt, b_fmt):
+    """N = 4096 with K = 7168 runs the grouped configurations' shape instances with an
+    E5M2 operand: equal to the oracle, and equal across every configuration of the layout
+    that runs E5M2 (planned or pinned)."""
+    info = {c["id"]: c for c in dg.dg_kernel_config_info()}
+    assert any(info[c]["shape_specialised"] for c in fmt_configs(layout))
+    outs = []
+    if layout == 1:
+        counts = [130, 0, 40]
+        cd = W.make_contiguous(counts, n=4096, k=7168, seed=71, a_fmt=a_fmt, b_fmt=b_fmt)
+        sentinel = np.full((cd["m_total"], 4096), W.SENTINEL_BF16, np.uint16)
+        ref = orc.m_grouped_contiguous(cd["a"], cd["sa"], cd["b"], cd["sb"], cd["m_indices"], d_init=sentinel,
+                                       a_fmt=a_fmt, b_fmt=b_fmt)
+        valid = cd["m_indices"] >= 0
+        for cfg in [-1] + fmt_configs(1):
+            say(f"contiguous {a_fmt}x{b_fmt} counts={counts} n=4096 k=7168 cfg={cfg}")
+            out = run_contiguous_fmt(cd, cfg)
+            assert np.all(out[~valid] == W.SENTINEL_BF16), "a padding row was written"
+            outs.append(out)
+        check_values(outs[0][valid], ref[valid], f"contiguous {a_fmt}x{b_fmt} n=4096 k=7168")
+    else:
+        mm = [0, 218, 77]
+        md = W.make_masked(3, 256, 4096, 7168, seed=72, masked_m=mm, a_fmt=a_fmt, b_fmt=b_fmt)
+        sentinel = np.full((3, 256, 4096), W.SENTINEL_BF16, np.uint16)
+        ref = orc.m_grouped_masked(md["a"], md["sa"], md["b"], md["sb"], md["masked_m"], d_init=sentinel,
+                                   a_fmt=a_fmt, b_fmt=b_fmt)
+        for cfg in [-1] + fmt_configs(2):
+            say(f"masked {a_fmt}x{b_fmt} masked_m={mm} n=4096 k=7168 cfg={cfg}")
+            out = run_masked_fmt(md, cfg)
+            for g, c in enumerate(mm):
+                assert np.all(out[g, c:] == W.SENTINEL_BF16), f"group {g}: a row >= masked_m was written"
+            outs.append(out)
+        valid = np.arange(256)[None, :] < np.array(mm)[:, None]
+        check_values(outs[0][valid], ref[valid], f"masked {a_fmt}x{b_fmt} n=4096 k=7168")
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
 def test_grouped_e4m3_pair_matches_plain_entries():
     import torch
     cd = W.make_contiguous([100, 40], n=96, k=256, seed=33)
