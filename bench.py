@@ -182,12 +182,21 @@ def cpu_baseline(w, data, target_s: float):
     oracle.build(force=False)
     cores = oracle.available_cores()
     a, sa, b, sb = data["a"], data["sa"], data["b"], data["sb"]
-    probe = 8
-    t0 = time.perf_counter()
-    oracle.gemm_fp8_nt(a[:probe], sa[:, :probe], b, sb, nthreads=cores)
-    dt = max(time.perf_counter() - t0, 1e-3)
-    rows = int(min(w.m, max(cores, probe * target_s / dt)))
-    rows = max(cores, rows - rows % cores)
+    # a call costs a fixed part (decoding B) plus a part per row: two probes (one and
+    # two rows per thread) separate them, then the sample is sized to about target_s
+    # (the whole workload when it fits), a whole number of rows per thread
+    def probe_s(nrows):
+        t0 = time.perf_counter()
+        oracle.gemm_fp8_nt(a[:nrows], sa[:, :nrows], b, sb, nthreads=cores)
+        return time.perf_counter() - t0
+    p1 = min(cores, w.m)
+    p2 = min(2 * p1, w.m)
+    t1, t2 = probe_s(p1), probe_s(p2)
+    per_row = max((t2 - t1) / max(p2 - p1, 1), t2 / p2 / 4, 1e-6)
+    fixed = max(t1 - per_row * p1, 0.0)
+    rows = int(min(w.m, max(p1, (target_s - fixed) / per_row)))
+    if rows < w.m:
+        rows = max(p1, rows - rows % cores)
     sel = np.linspace(0, w.m - 1, rows).astype(np.int64)
     t0 = time.perf_counter()
     oracle.gemm_fp8_nt(a[sel], sa[:, sel], b, sb, nthreads=cores)
