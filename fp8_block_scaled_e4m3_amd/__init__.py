@@ -369,6 +369,87 @@ def dg_check_contiguous_layout(m_indices, num_groups: int):
     return int(bad.value)
 
 
+# ---- the README's Python names ("deepseek-ai/deepgemm: clean and efficient FP8 GEMM
+# kernels", usage and utility paragraphs): the same calls, with operands passed as
+# (data, scale) pairs and the LHS scales as the README lays them out -- a [M, K/128]
+# tensor stored column-major (MN-major) with a 16-byte-aligned leading dimension, as
+# get_col_major_tma_aligned_tensor returns it.  Argument marshalling only.
+def _lhs_scales_mn_major(s, name):
+    """[.., M, K/128] column-major LHS scales -> the [.., K/128, ld] MN-major view the
+    dg_ calls take (no copy)."""
+    if s.stride(-2) != 1:
+        raise ValueError(f"{name}: the LHS scales must be column-major (MN-major): "
+                         "make them with get_col_major_tma_aligned_tensor")
+    return s.transpose(-1, -2)
+
+
+def set_num_sms(n: int) -> None:
+    """Cap the compute units the GEMMs may occupy (0: all)."""
+    dg_set_num_cus(n)
+
+
+def get_num_sms() -> int:
+    return dg_get_num_cus()
+
+
+def get_m_alignment_for_contiguous_layout() -> int:
+    return dg_get_m_alignment()
+
+
+def get_tma_aligned_size(x: int, element_size: int) -> int:
+    """``x`` elements of ``element_size`` bytes rounded up to a whole number of 16-byte
+    units (the leading dimension an MN-major scale tensor needs)."""
+    if element_size <= 0 or 16 % element_size:
+        raise ValueError("element_size must divide 16")
+    per = 16 // element_size
+    return -(-int(x) // per) * per
+
+
+def get_col_major_tma_aligned_tensor(x):
+    """fp32 scales ``x`` [M, K/128] (or [G, M, K/128]) -> the same values in a new tensor
+    of the same shape stored column-major with a 16-byte-aligned leading dimension (the
+    GPU transform kernel writes it)."""
+    squeeze = x.dim() == 2
+    xs = x.unsqueeze(0) if squeeze else x
+    if not xs.is_contiguous():
+        xs = xs.contiguous()
+    store = dg_transform_sa_mn_major(xs)                   # [G, K/128, ld]
+    rows = xs.shape[1]
+    view = store[:, :, :rows].transpose(1, 2)              # [G, M, K/128], column-major
+    return view[0] if squeeze else view
+
+
+def gemm_fp8_fp8_bf16_nt(lhs, rhs, out, stream=None) -> None:
+    """out[m, n] = bf16(lhs @ rhs^T) with lhs = (a [M, K] FP8, scales [M, K/128] fp32,
+    column-major) and rhs = (b [N, K] FP8, scales [N/128, K/128] fp32)."""
+    (a, sa), (b, sb) = lhs, rhs
+    dg_gemm_fp8_nt(a, _lhs_scales_mn_major(sa, "lhs"), b, sb, out, stream)
+
+
+def m_grouped_gemm_fp8_fp8_bf16_nt_contiguous(lhs, rhs, out, m_indices, stream=None) -> None:
+    """Contiguous layout: lhs = (a [M_total, K], scales [M_total, K/128] column-major),
+    rhs = (b [G, N, K], scales [G, N/128, K/128]), m_indices [M_total] (group or -1)."""
+    (a, sa), (b, sb) = lhs, rhs
+    dg_m_grouped_gemm_fp8_contiguous(a, _lhs_scales_mn_major(sa, "lhs"), b, sb, out, m_indices, stream)
+
+
+def m_grouped_gemm_fp8_fp8_bf16_nt_masked(lhs, rhs, out, masked_m, stream=None) -> None:
+    """Masked layout: lhs = (a [G, max_m, K], scales [G, max_m, K/128], each group
+    column-major), rhs = (b [G, N, K], scales [G, N/128, K/128]), masked_m [G] on the GPU."""
+    import torch
+    (a, sa), (b, sb) = lhs, rhs
+    mn = _lhs_scales_mn_major(sa, "lhs")                   # [G, K/128, max_m] view, stride (., ld, 1)
+    g, kb, max_m = mn.shape
+    ld = mn.stride(1)
+    if ld < max_m or mn.stride(0) != kb * ld:
+        raise ValueError("lhs scales: groups must be stacked as [G][K/128][ld] (get_col_major_tma_aligned_tensor)")
+    need = (mn.storage_offset() + g * kb * ld) * mn.element_size()
+    if mn.untyped_storage().nbytes() < need:
+        raise ValueError("lhs scales: the storage does not hold the padded leading dimension")
+    full = torch.as_strided(mn, (g, kb, ld), (kb * ld, ld, 1))
+    dg_m_grouped_gemm_fp8_masked(a, full, b, sb, out, masked_m, stream)
+
+
 # ---- tuning and introspection hooks (dg_tuning.h: outside the library's contract)
 def dg_set_kernel_config(config_id: int) -> None:
     """Pin a kernel configuration id for its layout (-1: automatic planning again)."""
@@ -419,4 +500,7 @@ __all__ = [
     "dg_quantize_fp8_128x128_fmt", "dg_get_aligned_ld_sa", "dg_transform_sa_mn_major",
     "dg_check_contiguous_layout", "dg_plan_tiles",
     "dg_set_kernel_config", "dg_kernel_config_info", "dg_describe_launch",
+    "gemm_fp8_fp8_bf16_nt", "m_grouped_gemm_fp8_fp8_bf16_nt_contiguous", "m_grouped_gemm_fp8_fp8_bf16_nt_masked",
+    "set_num_sms", "get_num_sms", "get_m_alignment_for_contiguous_layout", "get_tma_aligned_size",
+    "get_col_major_tma_aligned_tensor",
 ]

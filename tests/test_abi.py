@@ -293,3 +293,14 @@ def test_contiguous_layout_checker():
     assert dg.dg_check_contiguous_layout(bad, ng) == 385                  # ... but holds rows of group 3
     ok = mi.copy(); ok[130:140] = 0; ok[135] = -1                         # padding between rows of the group
     assert dg.dg_check_contiguous_layout(ok, ng) is None
+
+
+def test_readme_python_names_host_side():
+    """The README's utility names: the TMA-aligned size is the aligned ld_sa for fp32
+    scales (16 bytes), generic in the element size; the contiguous alignment is 128."""
+    for x in (1, 3, 4, 5, 301, 4096, 4097):
+        assert dg.get_tma_aligned_size(x, 4) == dg.dg_get_aligned_ld_sa(x)
+    assert dg.get_tma_aligned_size(10, 2) == 16 and dg.get_tma_aligned_size(16, 1) == 16
+    with pytest.raises(ValueError):
+        dg.get_tma_aligned_size(10, 3)
+    assert dg.get_m_alignment_for_contiguous_layout() == dg.dg_get_m_alignment() == 128
