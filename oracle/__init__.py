@@ -30,7 +30,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORC_LIB: load this already-built library instead (the mutation test points the pins
+# at copies of oracle.c with deliberate mistakes planted in them)
+_LIB_OVERRIDE = os.environ.get("ORC_LIB")
+_LIB = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 KBLOCK = 128
 
 _lib = None
@@ -39,22 +42,32 @@ _lib = None
 def build(force: bool = True) -> str:
     """Compile ``oracle.c`` into ``liboracle.so`` next to it (gcc, -O2, no fast-math,
     no FMA contraction so that every fp64 operation rounds exactly once)."""
+    if _LIB_OVERRIDE:
+        if force:
+            raise RuntimeError("ORC_LIB is set: the oracle library is given, not built")
+        return _LIB
     if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=gnu11", "-fPIC", "-shared", "-pthread",
-           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
-           _SRC, "-o", tmp, "-lm"]
-    subprocess.run(cmd, check=True)
+    compile_library(_SRC, tmp)
     os.replace(tmp, _LIB)
     return _LIB
+
+
+def compile_library(src: str, out: str) -> None:
+    """The one compile command of the oracle's C source (also used on planted-mistake
+    copies of it by the mutation test)."""
+    cmd = ["gcc", "-O2", "-std=gnu11", "-fPIC", "-shared", "-pthread",
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+           src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if not _LIB_OVERRIDE and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
         build()
     lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
