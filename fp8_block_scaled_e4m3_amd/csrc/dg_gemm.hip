@@ -489,8 +489,9 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // previous K block (its scales are still held), so the matrix core never
     // waits for a promotion and a block boundary costs no pipeline drain.
     // LDS stages: block kb lives in stage kb % NST.  In each block the single
-    // workgroup barrier sits at step JB: two steps after the last read of this
-    // block's stage (16x16 sub-tiles; the first MFMA of the last column for 32x32).
+    // workgroup barrier sits at step JB, shortly after the last read of this block's
+    // stage (16x16 sub-tiles: two steps after it, or, with the B fragment ring, at the
+    // first read of the next block's stage; the first MFMA of the last column for 32x32).
     // By then every wave has finished reading this block's stage, except for the
     // fragments already in registers, and has waited for its own copies of the
     // next block, so after the barrier
@@ -502,11 +503,20 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // tile's first blocks: their copies, A scales and fragments arrive while this
     // tile finishes, so a tile boundary costs no pipeline refill either.
     constexpr int NJ = FN * FM;
+    // B fragments are read ahead of their column: one column ahead when a column has
+    // three or more MFMAs (FM >= 3) to cover the LDS read; with fewer, PDC columns
+    // ahead into a ring of PDC + 1 registers, so that every read still has about three
+    // MFMAs to land.  Ring slot of column c of the block in stage U: (U*FN + c) % RB.
+    constexpr int PDC = MF == 16 && FM <= 2 ? ((3 + FM - 1) / FM < FN - 1 ? (3 + FM - 1) / FM : FN - 1) : 1;
+    constexpr bool BRING = PDC > 1;
+    constexpr int RB = PDC + 1;
+    static_assert(!BRING || (NST * FN) % RB == 0, "B fragment ring must tile the unrolled loop");
     // (the last read of this block's stage is the B fragment of the last column, at
-    // the first step of the column before it; an earlier barrier spreads the next
-    // block's first reads over more steps)
+    // the first step of column FN-1-PDC; the barrier sits at or before the step whose
+    // read-ahead first reaches the next block's stage (column FN-PDC); for FM >= 3 an
+    // earlier barrier spreads the next block's first reads over more steps)
     constexpr int EARLY = MF == 16 && FM > 2 ? FM - 2 : 0;
-    constexpr int JB = (FN - 1) * FM - EARLY;
+    constexpr int JB = BRING ? (FN - PDC) * FM : (FN - 1) * FM - EARLY;
     static_assert(FN >= 2, "the barrier sits in the last of at least two columns");
     // ring of in-flight partials: its position is a compile-time function of the
     // step because the block loop is unrolled by NST
@@ -557,6 +567,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     using std::integral_constant;
     constexpr int NH = MF == 32 ? 2 : 1;
     v8i af[FM][NH], bf[NH], bnext;
+    v8i bq[RB];                                // B fragment ring (BRING)
     vacc part[R];
     vacc acc[FM][FN];
     const int arow0 = wm * WTM, bcol0 = BM + wn * WTN;
@@ -593,7 +604,12 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         lane_base(smem0, bcol0, lb);
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-            bf[h] = frag(lb, 0, h);
+            if constexpr (BRING) {
+#pragma unroll
+                for (int c = 0; c < PDC; ++c) bq[c] = frag(lb, c * MF, 0);
+            } else {
+                bf[h] = frag(lb, 0, h);
+            }
             if (h == 0) read_sa(sc[0], smem0);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) af[fm][h] = frag(la, fm * MF, h);
@@ -706,7 +722,21 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         for (int j = 0; j < NJ; ++j) {
             const int fn = j / FM, fm = j % FM;
             const int slot = (U * NJ + j) % R;
-            if constexpr (MF == 16) {
+            if constexpr (MF == 16 && BRING) {
+                part[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[(U * FN + fn) % RB], af[fm][0], vacc{},
+                                                                              FMT_SRC0, FMT_SRC1, 0, 0, 0, 0);
+                promote(j - kLag, 0, NACC);
+                issue_loads(j);
+                if (j == JB) barrier();
+                // column fn + PDC (of the next block's stage past the last column), into
+                // the slot of column fn - 1, whose MFMAs are all issued
+                if (fm == 0) {
+                    const int c = fn + PDC;
+                    bq[(U * FN + c) % RB] = c < FN ? frag(lc, c * MF, 0) : frag(ln, (c - FN) * MF, 0);
+                }
+                if (j == JB) read_sa(scn, nxt);
+                if (fn == FN - 1) af[fm][0] = frag(lna, fm * MF, 0);
+            } else if constexpr (MF == 16) {
                 part[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[0], af[fm][0], vacc{}, FMT_SRC0, FMT_SRC1,
                                                                               0, 0, 0, 0);
                 promote(j - kLag, 0, NACC);
