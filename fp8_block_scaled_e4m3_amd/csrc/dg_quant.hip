@@ -104,6 +104,34 @@ __device__ __forceinline__ bool any_nan(const float* v, int n) {
     return r;
 }
 
+// Maximum over each aligned group of L lanes (L = 16 or 32) of non-negative, non-NaN
+// values, through the cross-lane paths of the vector ALU rather than LDS: DPP lane
+// swaps within quads (lanes 1 and 2 apart), mirrors within 8- and 16-lane rows, and
+// for L = 32 the swap of adjacent 16-lane rows.  Each step combines every lane with a
+// lane of the other half of its current span, so after log2(L) steps every lane of a
+// group holds the group's maximum.  Non-negative floats (+0 to +inf) order like their
+// bit patterns read as signed integers, so the steps take integer maxima.
+template <int CTRL>
+__device__ __forceinline__ int dpp_max_bits(int x) {
+    const int o = __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+    return o > x ? o : x;
+}
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(L == 16 || L == 32, "group of 16 or 32 lanes");
+    int b = __builtin_bit_cast(int, v);
+    b = dpp_max_bits<0xB1>(b);    // quad_perm [1,0,3,2]
+    b = dpp_max_bits<0x4E>(b);    // quad_perm [2,3,0,1]
+    b = dpp_max_bits<0x141>(b);   // row_half_mirror
+    b = dpp_max_bits<0x140>(b);   // row_mirror
+    if constexpr (L == 32) {
+        const auto sw = __builtin_amdgcn_permlane16_swap((unsigned)b, (unsigned)b, false, false);
+        const int lo = (int)sw[0], hi = (int)sw[1];
+        b = lo > hi ? lo : hi;
+    }
+    return __builtin_bit_cast(float, b);
+}
+
 // one decision for the whole wave, so the paths never diverge inside it
 __device__ __forceinline__ bool wave_all(bool b) { return __ballot(!b) == 0; }
 
@@ -157,12 +185,7 @@ quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, Div
     for (int r = 0; r < kRowsPerThread; ++r) {
         const unsigned g = g0 + r * GPW;
         if (g >= groups_total) break;                   // uniform over the L lanes of a group
-        float amax = amax_of(v[r], N, 0.f);
-#pragma unroll
-        for (int off = L / 2; off >= 1; off >>= 1) {
-            const float o = __shfl_xor(amax, off, L);
-            amax = o > amax ? o : amax;
-        }
+        const float amax = group_max<L>(amax_of(v[r], N, 0.f));
         const float scale = block_scale<FMT>(amax);
         const unsigned row = div_u32(g, kdiv), kb = g - row * (unsigned)kblocks;
         const bool fast = wave_all(fast_scale(scale) && !any_nan(v[r], N));
