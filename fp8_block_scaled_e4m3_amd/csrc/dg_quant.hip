@@ -157,40 +157,65 @@ __device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 f) {
 
 // 1x128: a 128-element row block is read by L = 128/N lanes with one 16-byte load
 // each (the block's bytes are contiguous, so every load instruction is coalesced).
-// A thread handles kRowsPerThread row blocks of one K block, their loads all in
-// flight before any is reduced.  Blocks are numbered K block fastest, so a
-// workgroup reads long contiguous stretches of each row.
+// A thread handles kRowsPerThread row blocks, their loads all in flight before any
+// is reduced.  Blocks are numbered K block fastest, so a workgroup reads long
+// contiguous stretches of each row.  RUN (when kRowsPerThread divides K/128): a
+// thread's blocks are consecutive K blocks of one row, so one row split and one
+// address serve all of them (the split and the 64-bit addressing are a large share
+// of this kernel's vector instructions); otherwise they are GPW blocks apart and each
+// finds its own row.
 constexpr int kRowsPerThread = 4;
 
-template <typename T, int FMT>
+template <typename T, int FMT, bool RUN>
 __global__ void __launch_bounds__(256)
 quant_1x128_kernel(const T* __restrict__ x, long ldx, int rows, int kblocks, DivU32 kdiv, uint8_t* __restrict__ q,
                    long ldq, float* __restrict__ sa, long ld_sa) {
     constexpr int N = Vec<T>::N, L = kQBlock / N, GPW = 256 / L;   // groups of L lanes per workgroup
+    constexpr int R = kRowsPerThread;
     const int lg = threadIdx.x % L, grp = threadIdx.x / L;
-    // workgroup w handles groups [w*GPW*R, (w+1)*GPW*R); group g = (row, kb) with kb
-    // fastest (the host keeps rows * kblocks below 2^31)
+    // (the host keeps rows * kblocks below 2^31)
     const unsigned groups_total = (unsigned)rows * (unsigned)kblocks;
-    const unsigned g0 = blockIdx.x * (unsigned)(GPW * kRowsPerThread) + grp;
-    float v[kRowsPerThread][N];
+    float v[R][N];
+    if constexpr (RUN) {
+        // run G = blocks [G*R, G*R + R) of one row; kdiv divides by kblocks / R
+        const unsigned G = blockIdx.x * (unsigned)GPW + grp;
+        if (G * R >= groups_total) return;              // uniform over the L lanes of a group
+        const unsigned row = div_u32(G, kdiv), kb0 = (G - row * (unsigned)(kblocks / R)) * R;
+        const T* xb = x + (long)row * ldx + kb0 * kQBlock + lg * N;
 #pragma unroll
-    for (int r = 0; r < kRowsPerThread; ++r) {
-        const unsigned g = g0 + r * GPW;
-        if (g < groups_total) {
-            const unsigned row = div_u32(g, kdiv), kb = g - row * (unsigned)kblocks;
-            Vec<T>::load(x + (long)row * ldx + kb * kQBlock + lg * N, v[r]);
+        for (int r = 0; r < R; ++r) Vec<T>::load(xb + r * kQBlock, v[r]);
+        uint8_t* qb = q + (long)row * ldq + kb0 * kQBlock + lg * N;
+        float* sb = sa + (long)kb0 * ld_sa + row;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float amax = group_max<L>(amax_of(v[r], N, 0.f));
+            const float scale = block_scale<FMT>(amax);
+            const bool fast = wave_all(fast_scale(scale) && !any_nan(v[r], N));
+            store_codes<N, FMT>(qb + r * kQBlock, v[r], scale, fast);
+            if (lg == 0) sb[r * ld_sa] = scale;
         }
-    }
+    } else {
+        // workgroup w handles groups [w*GPW*R, (w+1)*GPW*R); group g = (row, kb)
+        const unsigned g0 = blockIdx.x * (unsigned)(GPW * R) + grp;
 #pragma unroll
-    for (int r = 0; r < kRowsPerThread; ++r) {
-        const unsigned g = g0 + r * GPW;
-        if (g >= groups_total) break;                   // uniform over the L lanes of a group
-        const float amax = group_max<L>(amax_of(v[r], N, 0.f));
-        const float scale = block_scale<FMT>(amax);
-        const unsigned row = div_u32(g, kdiv), kb = g - row * (unsigned)kblocks;
-        const bool fast = wave_all(fast_scale(scale) && !any_nan(v[r], N));
-        store_codes<N, FMT>(q + (long)row * ldq + kb * kQBlock + lg * N, v[r], scale, fast);
-        if (lg == 0) sa[(long)kb * ld_sa + row] = scale;
+        for (int r = 0; r < R; ++r) {
+            const unsigned g = g0 + r * GPW;
+            if (g < groups_total) {
+                const unsigned row = div_u32(g, kdiv), kb = g - row * (unsigned)kblocks;
+                Vec<T>::load(x + (long)row * ldx + kb * kQBlock + lg * N, v[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const unsigned g = g0 + r * GPW;
+            if (g >= groups_total) break;                   // uniform over the L lanes of a group
+            const float amax = group_max<L>(amax_of(v[r], N, 0.f));
+            const float scale = block_scale<FMT>(amax);
+            const unsigned row = div_u32(g, kdiv), kb = g - row * (unsigned)kblocks;
+            const bool fast = wave_all(fast_scale(scale) && !any_nan(v[r], N));
+            store_codes<N, FMT>(q + (long)row * ldq + kb * kQBlock + lg * N, v[r], scale, fast);
+            if (lg == 0) sa[(long)kb * ld_sa + row] = scale;
+        }
     }
 }
 
@@ -279,21 +304,29 @@ template <int FMT>
 hipError_t launch_1x128(const void* x, int x_bf16, long ldx, int rows, int k, uint8_t* q, long ldq, float* sa,
                         long ld_sa, hipStream_t stream) {
     const int kblocks = k / kQBlock;
-    const DivU32 kdiv = make_div_u32((uint32_t)kblocks);
+    const bool run = kblocks % kRowsPerThread == 0;
+    const DivU32 kdiv = make_div_u32((uint32_t)(run ? kblocks / kRowsPerThread : kblocks));
     const long per_wg = (x_bf16 ? 256 / 16 : 256 / 32) * (long)kRowsPerThread;   // groups per workgroup
     // row chunks small enough for 32-bit group indices inside the kernel
     const long chunk = ((1l << 30) / kblocks) > 0 ? ((1l << 30) / kblocks) : 1;
     for (long r0 = 0; r0 < rows; r0 += chunk) {
         const int nr = (int)(rows - r0 < chunk ? rows - r0 : chunk);
         const long blocks = ((long)nr * kblocks + per_wg - 1) / per_wg;
-        if (x_bf16)
-            hipLaunchKernelGGL((quant_1x128_kernel<uint16_t, FMT>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                               static_cast<const uint16_t*>(x) + r0 * ldx, ldx, nr, kblocks, kdiv, q + r0 * ldq,
-                               ldq, sa + r0, ld_sa);
+        const uint16_t* xh = static_cast<const uint16_t*>(x) + r0 * ldx;
+        const float* xf = static_cast<const float*>(x) + r0 * ldx;
+        const dim3 grid((unsigned)blocks);
+        if (x_bf16 && run)
+            hipLaunchKernelGGL((quant_1x128_kernel<uint16_t, FMT, true>), grid, dim3(256), 0, stream, xh, ldx, nr,
+                               kblocks, kdiv, q + r0 * ldq, ldq, sa + r0, ld_sa);
+        else if (x_bf16)
+            hipLaunchKernelGGL((quant_1x128_kernel<uint16_t, FMT, false>), grid, dim3(256), 0, stream, xh, ldx, nr,
+                               kblocks, kdiv, q + r0 * ldq, ldq, sa + r0, ld_sa);
+        else if (run)
+            hipLaunchKernelGGL((quant_1x128_kernel<float, FMT, true>), grid, dim3(256), 0, stream, xf, ldx, nr,
+                               kblocks, kdiv, q + r0 * ldq, ldq, sa + r0, ld_sa);
         else
-            hipLaunchKernelGGL((quant_1x128_kernel<float, FMT>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                               static_cast<const float*>(x) + r0 * ldx, ldx, nr, kblocks, kdiv, q + r0 * ldq, ldq,
-                               sa + r0, ld_sa);
+            hipLaunchKernelGGL((quant_1x128_kernel<float, FMT, false>), grid, dim3(256), 0, stream, xf, ldx, nr,
+                               kblocks, kdiv, q + r0 * ldq, ldq, sa + r0, ld_sa);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

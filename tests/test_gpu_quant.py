@@ -75,7 +75,9 @@ def same_bits(a, b):
     return np.array_equal(np.asarray(a).view(np.uint32), np.asarray(b).view(np.uint32))
 
 
-@pytest.mark.parametrize("rows,k", [(1, 128), (7, 384), (300, 640), (129, 1024)])
+# K/128 = 1, 3, 5: a thread's blocks lie GPW blocks apart; 8, 12: runs of four
+# consecutive K blocks per thread (33 x 12 blocks leaves a partial last workgroup)
+@pytest.mark.parametrize("rows,k", [(1, 128), (7, 384), (300, 640), (129, 1024), (33, 1536)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 def test_quant_1x128_bit_exact(orc, rows, k, dtype, fmt):
