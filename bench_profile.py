@@ -56,7 +56,10 @@ PMC_PASSES = {
                  "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_VMEM", "GRBM_GUI_ACTIVE"],
     "fetch": ["FETCH_SIZE"],
     "write": ["WRITE_SIZE"],
+    "lds": ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL", "SQ_INSTS_LDS_STORE_BANDWIDTH",
+            "SQ_WAIT_ANY", "TA_BUSY_avr", "GRBM_GUI_ACTIVE"],
 }
+OPTIONAL_PASSES = ("lds",)
 
 
 def say(*a):
@@ -95,10 +98,15 @@ def collect(args) -> int:
     pbench = bench + (["--no-cpu-baseline"] if "--no-cpu-baseline" not in bench else [])
     for pname, ctrs in PMC_PASSES.items():
         pdir = os.path.join(out, "pmc_" + pname)
+        # a counter pass over the bench takes seconds; a refused counter set can hang
         rc = run_step(f"pmc {pname}", ["rocprofv3", "--pmc"] + ctrs + ["--kernel-include-regex", KERNEL_REGEX,
                                                                         "-f", "csv", "-d", pdir, "-o", "run", "--"]
-                      + pbench, args.limit, os.path.join(out, f"pmc_{pname}.log"))
+                      + pbench, min(args.limit, 150), os.path.join(out, f"pmc_{pname}.log"))
         meta["passes"][pname] = {"counters": ctrs, "rc": rc}
+        if rc != 0 and pname in OPTIONAL_PASSES:
+            say(f"profile: optional pass {pname} failed (rc {rc}); its counters are left out")
+            rc = 0
+            continue
         if rc != 0:
             break
     # 3. copy calibration of the byte counters
@@ -335,6 +343,24 @@ def summarize(args) -> int:
             bc = cmean("sq_stall", "SQ_LDS_BANK_CONFLICT")
             if bc is not None:
                 derived.append(("LDS bank-conflict cycles", f"{bc:.0f}"))
+            # LDS pass: indexed-access cycles (fragment reads; the copies' direct-to-LDS
+            # writes are not indexed accesses), full command/data queues, the texture
+            # address unit's busy cycles averaged over its instances
+            g3 = cmean("lds", "GRBM_GUI_ACTIVE")
+            if g3:
+                cyc = g3 / 8 * 256
+                for ctr, label in (("SQ_LDS_IDX_ACTIVE", "LDS busy, indexed accesses (LDS_IDX_ACTIVE / (GUI_ACTIVE/8 * 256 CUs))"),
+                                   ("SQ_LDS_CMD_FIFO_FULL", "LDS command queue full (LDS_CMD_FIFO_FULL / (GUI_ACTIVE/8 * 256 CUs))"),
+                                   ("SQ_LDS_DATA_FIFO_FULL", "LDS data queue full (LDS_DATA_FIFO_FULL / (GUI_ACTIVE/8 * 256 CUs))")):
+                    v = cmean("lds", ctr)
+                    if v is not None:
+                        derived.append((label, f"{100 * v / cyc:.1f} %"))
+                sb = cmean("lds", "SQ_INSTS_LDS_STORE_BANDWIDTH")
+                if sb is not None:
+                    derived.append(("LDS store bytes per CU per clock (LDS_STORE_BANDWIDTH*64 / ...)", f"{sb * 64 / cyc:.1f}"))
+                ta = cmean("lds", "TA_BUSY_avr")
+                if ta is not None:
+                    derived.append(("texture address unit busy (TA_BUSY_avr / (GUI_ACTIVE/8))", f"{100 * ta / (g3 / 8):.1f} %"))
             fs, ws = cmean("fetch", "FETCH_SIZE"), cmean("write", "WRITE_SIZE")
             alg = None
             if kind == "headline":

@@ -59,7 +59,8 @@ def _synthetic_run(d, n=25):
     """Headline: 131072 x 512, 200 us, 2.0 GHz, MFMA busy 50 %, 100000 KiB fetched and 50000 KiB
     written per dispatch.  Cast: a two-dimensional grid (14336 x 56) in the trace, the same
     802816 work-items as one number in the counters.  Copy calibration: 1 GiB copied reads
-    as 524288 KiB fetched (factor 2) and 1048576 KiB written (factor 1)."""
+    as 524288 KiB fetched (factor 2) and 1048576 KiB written (factor 1).  LDS pass: 40 % indexed-busy,
+    queues full 10 % and 5 % of the cycles, 20 store bytes per clock, texture unit 30 % busy."""
     with open(os.path.join(d, "meta.json"), "w") as f:
         json.dump({"bench_cmd": ["python3", "bench.py", "--gpus", "1", "--steps", "20", "--warmup", "5"]}, f)
     line = {"metric": "m", "config": {"workload": "dense_m4096_n7168_k7168"},
@@ -81,6 +82,9 @@ def _synthetic_run(d, n=25):
         "sq_stall": {"GRBM_GUI_ACTIVE": gui, "SQ_ACTIVE_INST_VALU": 0.25 * gui / 8 * 256},
         "fetch": {"FETCH_SIZE": 100000.0},
         "write": {"WRITE_SIZE": 50000.0},
+        "lds": {"GRBM_GUI_ACTIVE": gui, "SQ_LDS_IDX_ACTIVE": 0.4 * gui / 8 * 256,
+                "SQ_LDS_CMD_FIFO_FULL": 0.1 * gui / 8 * 256, "SQ_LDS_DATA_FIFO_FULL": 0.05 * gui / 8 * 256,
+                "SQ_INSTS_LDS_STORE_BANDWIDTH": 20.0 * gui / 8 * 256 / 64, "TA_BUSY_avr": 0.3 * gui / 8},
     }
     for pname, vals in passes.items():
         rows, did, t = [], 1, 1_000_000
@@ -119,6 +123,11 @@ def test_profile_summary_of_a_synthetic_run(tmp_path):
     assert "grid: 802816 work-items, workgroup 256" in cast
     assert "HBM bytes read (FETCH_SIZE KiB x 1024 x copy factor 2.000): 20.5 MB" in cast
     assert "upper bound" not in head
+    assert "LDS busy, indexed accesses (LDS_IDX_ACTIVE / (GUI_ACTIVE/8 * 256 CUs)): 40.0 %" in head
+    assert "LDS command queue full (LDS_CMD_FIFO_FULL / (GUI_ACTIVE/8 * 256 CUs)): 10.0 %" in head
+    assert "LDS data queue full (LDS_DATA_FIFO_FULL / (GUI_ACTIVE/8 * 256 CUs)): 5.0 %" in head
+    assert "LDS store bytes per CU per clock (LDS_STORE_BANDWIDTH*64 / ...): 20.0" in head
+    assert "texture address unit busy (TA_BUSY_avr / (GUI_ACTIVE/8)): 30.0 %" in head
     rec = json.loads((out / "hbm_traffic.json").read_text())
     assert rec["calibration"]["fetch_factor"] == pytest.approx(2.0)
     assert rec["calibration"]["write_factor"] == pytest.approx(1.0)
