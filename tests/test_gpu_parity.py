@@ -82,6 +82,38 @@ def test_dense_ragged_shapes(orc, m, n, k):
         assert np.array_equal(o, outs[0])
 
 
+@pytest.mark.parametrize("m,n,k", [(300, 400, 640), (64, 7168, 2048)])
+def test_dense_strided_operands(orc, m, n, k):
+    """A, B, sA and D as views into wider buffers (row strides lda = K + 256, ldb = K + 128,
+    ld_sa = the aligned M + 8, ldd = N + 24): the same bits as with packed operands on
+    every configuration, the oracle's values, and nothing written between rows."""
+    import torch
+    dd = W.make_dense(m, n, k, seed=m + n + k)
+    ref = oracle_dense(orc, dd)
+    packed, _ = run_dense(dd)
+    check_values(packed, ref, f"dense packed {m}x{n}x{k}")
+    lda, ldb, ld_sa, ldd = k + 256, k + 128, dd["sa"].shape[1] + 8, n + 24
+    a_buf = torch.zeros((m, lda), dtype=torch.uint8, device="cuda:0")
+    b_buf = torch.zeros((n, ldb), dtype=torch.uint8, device="cuda:0")
+    sa_buf = torch.zeros((k // 128, ld_sa), dtype=torch.float32, device="cuda:0")
+    a_buf[:, :k] = to_dev(dd["a"])
+    b_buf[:, :k] = to_dev(dd["b"])
+    sa_buf[:, :dd["sa"].shape[1]] = to_dev(dd["sa"])
+    sb = to_dev(dd["sb"])
+    for cfg in [-1] + configs_of(0):
+        d_buf = sentinel_like((m, ldd))
+        say(f"dense strided {m}x{n}x{k} cfg={cfg}")
+        dg.dg_set_kernel_config(cfg)
+        try:
+            dg.dg_gemm_fp8_nt(a_buf[:, :k], sa_buf[:, :m], b_buf[:, :k], sb, d_buf[:, :n])
+            torch.cuda.synchronize()
+        finally:
+            dg.dg_set_kernel_config(-1)
+        fb = bits(d_buf)
+        assert np.array_equal(fb[:, :n], packed), f"strided operands changed the result (cfg {cfg})"
+        assert np.all(fb[:, n:] == W.SENTINEL_BF16), "a column between rows was written"
+
+
 def test_dense_under_filled_workload_full_compare(orc):
     dd = W.make(W.WORKLOADS["dense_m256_n7168_k2048"])
     say("dense 256x7168x2048 (planned config)", dg.dg_describe_launch(0, 256, 7168, 2048, 1))
