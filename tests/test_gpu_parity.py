@@ -384,6 +384,22 @@ def test_masked_edges_all_configs(orc, max_m):
         assert np.array_equal(dense, outs[0][g, :mm[g]])
 
 
+def test_masked_capacity_beyond_one_row_block(orc):
+    """A capacity of 600 rows spans three 256-row blocks (and five 128-row ones): counts
+    at and around the block edges, every masked configuration bit-identical, within
+    tolerance of the oracle, rows at or past masked_m untouched."""
+    mm = [0, 600, 1, 255, 256, 257, 511, 512, 599, 384]
+    md = W.make_masked(len(mm), 600, 144, 384, seed=71, masked_m=mm)
+    outs = []
+    for cfg in configs_of(2):
+        say(f"masked capacity 600 counts={mm} cfg={cfg}")
+        out = run_masked(md, cfg)
+        check_masked(orc, md, out)
+        outs.append(out)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
 def test_masked_shape_instance_all_configs(orc):
     """N = 4096 with K = 7168 runs the instance compiled for that shape in the masked
     configurations that have one: every masked configuration gives the same bits,
