@@ -518,11 +518,25 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // tile's first blocks: their copies, A scales and fragments arrive while this
     // tile finishes, so a tile boundary costs no pipeline refill either.
     constexpr int NJ = FN * FM;
+    // ring of in-flight partials: its position is a compile-time function of the
+    // step because the block loop is unrolled by NST
+    constexpr int R = MF == 32 ? 2
+                    : ((NST * NJ) % 4 == 0 ? 4 : ((NST * NJ) % 3 == 0 ? 3 : 2));
+    static_assert((NST * NJ) % R == 0, "partial ring must tile the unrolled loop");
+    constexpr int kLag = R - 1;
     // B fragments are read ahead of their column: one column ahead when a column has
     // three or more MFMAs (FM >= 3) to cover the LDS read; with fewer, PDC columns
     // ahead into a ring of PDC + 1 registers, so that every read still has about three
     // MFMAs to land.  Ring slot of column c of the block in stage U: (U*FN + c) % RB.
-    constexpr int PDC = MF == 16 && FM <= 2 ? ((3 + FM - 1) / FM < FN - 1 ? (3 + FM - 1) / FM : FN - 1) : 1;
+    // (Shortened where a longer ring would not tile the loop unrolled over NST blocks,
+    // or would put the barrier before the promotions that still need the previous
+    // block's scales.)
+    constexpr int PDC = [] {
+        if (!(MF == 16 && FM <= 2)) return 1;
+        int d = (3 + FM - 1) / FM < FN - 1 ? (3 + FM - 1) / FM : FN - 1;
+        while (d > 1 && ((NST * FN) % (d + 1) != 0 || (FN - d) * FM < kLag)) --d;
+        return d;
+    }();
     constexpr bool BRING = PDC > 1;
     constexpr int RB = PDC + 1;
     static_assert(!BRING || (NST * FN) % RB == 0, "B fragment ring must tile the unrolled loop");
@@ -533,12 +547,6 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     constexpr int EARLY = MF == 16 && FM > 2 ? FM - 2 : 0;
     constexpr int JB = BRING ? (FN - PDC) * FM : (FN - 1) * FM - EARLY;
     static_assert(FN >= 2, "the barrier sits in the last of at least two columns");
-    // ring of in-flight partials: its position is a compile-time function of the
-    // step because the block loop is unrolled by NST
-    constexpr int R = MF == 32 ? 2
-                    : ((NST * NJ) % 4 == 0 ? 4 : ((NST * NJ) % 3 == 0 ? 3 : 2));
-    static_assert((NST * NJ) % R == 0, "partial ring must tile the unrolled loop");
-    constexpr int kLag = R - 1;
     constexpr int NVM = NSLOT + 1;             // vector memory instructions per block
     // Copies of block kb + NST (NSLOT operand slots, then the A-scale copy) go to
     // stage kb % NST as soon as block kb's barrier has freed it: copy t at step
