@@ -51,6 +51,9 @@ int main() {
     CHECK(dg::g_last_config == 3 && g_last_params.num_tiles == 256 && dg::g_last_grid == 256);
     CHECK(dense(128, 128, 512) == DG_OK);
     CHECK(g_last_params.num_tiles >= 1 && dg::g_last_grid == g_last_params.num_tiles);
+    // small M at K = 7168: 64x64 tiles fill more CUs than 64x112 in the same single round
+    CHECK(dense(64, 4096, 7168) == DG_OK);
+    CHECK(dg::g_last_config == 6 && g_last_params.num_tiles == 64 && dg::g_last_grid == 64);
     // ---- dense validation, nothing launched on failure
     const int before = dg::g_launches;
     CHECK(dense(128, 128, 200) == DG_ERR_UNSUPPORTED);                // K % 128
@@ -127,7 +130,7 @@ int main() {
     int info[7];
     int ninfo = 0;
     while (dg_kernel_config_info(ninfo, info) == DG_OK) ++ninfo;
-    CHECK(ninfo == 15);
+    CHECK(ninfo == 16);
 
     // ---- casts and the sA helpers
     const int aux = dg::g_aux_launches;
