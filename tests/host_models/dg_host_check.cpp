@@ -102,6 +102,11 @@ int main() {
     CHECK(dg_m_grouped_gemm_fp8_masked(P(0x1000), F(0x2000), 256, P(0x3000), F(0x4000), P(0x5000), I(0x6000), 16,
                                        256, 4096, 7168, nullptr) == DG_OK);
     CHECK(dg::g_last_grid <= 192 && dg::g_last_config == 20);
+    // capacity of at most 128 rows: the 128x256 tile (each B tile streamed once, half the A re-reads of 128x128)
+    CHECK(dg_set_num_cus(0) == DG_OK);
+    CHECK(dg_m_grouped_gemm_fp8_masked(P(0x1000), F(0x2000), 128, P(0x3000), F(0x4000), P(0x5000), I(0x6000), 8,
+                                       128, 7168, 2048, nullptr) == DG_OK);
+    CHECK(dg::g_last_config == 23 && g_last_params.num_tiles == 8 * 28);
     CHECK(dg_set_num_cus(3) == DG_OK);
     CHECK(dense(4096, 7168, 7168) == DG_OK && dg::g_last_grid == 3 && g_last_params.xcd_remap == 0);
     CHECK(dg_set_num_cus(0) == DG_OK && dg_get_num_cus() == 256);
