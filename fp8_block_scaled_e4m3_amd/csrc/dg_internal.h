@@ -63,7 +63,7 @@ constexpr int kNumSpecShapes = sizeof(kSpecShapes) / sizeof(kSpecShapes[0]);
     X(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false, true, true)             \
     X(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true, false, false)           \
     X(5, kDense, 256, 256, 4, 2, 16, 2, 1.15, true, true, true)             \
-    X(6, kDense, 64, 64, 4, 1, 16, 4, 0.32, false, false, false)            \
+    X(6, kDense, 64, 64, 4, 1, 16, 4, 0.32, false, true, false)             \
     /* contiguous (BLOCK_M = the 128-row segment alignment, or two of them) */ \
     X(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false, false, false)    \
     X(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false, true, false)     \
@@ -73,7 +73,7 @@ constexpr int kNumSpecShapes = sizeof(kSpecShapes) / sizeof(kSpecShapes[0]);
     X(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false, false, false)        \
     X(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false, true, false)         \
     X(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false, false, false)        \
-    X(23, kMasked, 128, 256, 2, 4, 16, 3, 1.15, false, false, false)        \
+    X(23, kMasked, 128, 256, 2, 4, 16, 3, 1.15, false, true, false)         \
     X(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, true, true)
 
 // Table of compiled configurations (defined in dg_gemm.hip).
