@@ -33,10 +33,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the library sources with comments and blank space removed, so that the
-    stored traffic counters stay valid across comment edits and lapse on code edits."""
+    """Hash of the library sources with comments and blank space removed, and of the
+    code-generation flags, so that the stored traffic counters stay valid across comment
+    edits and lapse on code or code-generation changes."""
     import re
+    from fp8_block_scaled_e4m3_amd.build import CODEGEN_FLAGS
     h = hashlib.sha256()
+    h.update(" ".join(CODEGEN_FLAGS).encode())
     for name in ("dg_gemm.hip", "dg_quant.hip", "dg_internal.h", "dg_api.cpp"):
         with open(os.path.join(ROOT, "fp8_block_scaled_e4m3_amd", "csrc", name), encoding="utf-8") as f:
             text = f.read()
