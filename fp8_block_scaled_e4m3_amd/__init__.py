@@ -459,11 +459,12 @@ def dg_set_kernel_config(config_id: int) -> None:
 def dg_kernel_config_info() -> list:
     """All compiled kernel configurations as dicts (id, layout, block_m, block_n, waves,
     all_formats: whether E5M2 operands run in it, shape_specialised: whether it has
-    instances compiled for fixed N and K)."""
-    out, res, i = (ctypes.c_int * 7)(), [], 0
+    instances compiled for fixed N and K, k_groups: 2 where two wave groups each sum
+    every other K block and the sums are added at the end, else 1)."""
+    out, res, i = (ctypes.c_int * 8)(), [], 0
     while load_library().dg_kernel_config_info(i, out) == DG_OK:
-        res.append(dict(zip(("id", "layout", "block_m", "block_n", "waves", "all_formats", "shape_specialised"),
-                            list(out))))
+        res.append(dict(zip(("id", "layout", "block_m", "block_n", "waves", "all_formats", "shape_specialised",
+                             "k_groups"), list(out))))
         i += 1
     return res
 

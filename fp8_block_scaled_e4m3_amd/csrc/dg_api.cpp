@@ -163,9 +163,15 @@ int raster_group_m(int tiles_m, int tiles_n, long chunk, int bm, int bn) {
     return best;
 }
 
+// K groups (two groups of waves splitting a tile's K blocks) shorten each tile's chain
+// of block steps but add a second wave per SIMD and a reduction: they paid only where
+// the tiles leave CUs idle or just fill them and K is long (64x4096x7168 and
+// 128x7168x7168: 11-12% faster), and lost at K = 2048 and with more tiles than CUs.
+constexpr int kKGroupMinKBlocks = 32;
+
 // Pick among the compiled configurations of one layout.
 int choose_config(int layout, int m, int n, int num_groups, int fmt, int num_units, const DeviceInfo* dev,
-                  int max_m_hint) {
+                  int max_m_hint, int kblocks) {
     int count = 0;
     const KernelConfig* cfgs = dg::kernel_configs(&count);
     const int forced = g_forced_cfg[layout];
@@ -184,6 +190,7 @@ int choose_config(int layout, int m, int n, int num_groups, int fmt, int num_uni
         // The busiest CU's share: ceil(tiles / CUs) tiles of bm x bn at the shape's
         // relative throughput (workgroups resident together share one CU).
         const long tiles = (layout == dg::kMasked ? num_groups : 1) * ceil_div(m, c.bm) * ceil_div(n, c.bn);
+        if (c.wk > 1 && (tiles > num_units || kblocks < kKGroupMinKBlocks)) continue;
         const long waves = ceil_div(tiles, (long)num_units);
         const double cost = (double)waves * c.bm * c.bn / c.eff;
         if (best < 0 || better(cost, waves, best_cost, best_waves)) {
@@ -207,7 +214,7 @@ int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_
     }
     int count = 0;
     const KernelConfig* cfgs = dg::kernel_configs(&count);
-    const int ci = choose_config(layout, m_for_plan, p.n, p.num_groups, p.fmt, units, dev, max_m_hint);
+    const int ci = choose_config(layout, m_for_plan, p.n, p.num_groups, p.fmt, units, dev, max_m_hint, p.kblocks);
     if (ci < 0) return DG_ERR_UNSUPPORTED;
     const KernelConfig& c = cfgs[ci];
     const int per_cu = dev ? dev->occ[ci] : 1;
@@ -228,7 +235,7 @@ int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_
     if (describe_out) {
         describe_out[0] = c.bm;
         describe_out[1] = c.bn;
-        describe_out[2] = c.wm * c.wn;
+        describe_out[2] = c.wm * c.wn * c.wk;
         describe_out[3] = p.num_tiles;
         describe_out[4] = (int)grid;
         describe_out[5] = c.id;
@@ -238,7 +245,7 @@ int launch(int layout, GemmParams& p, int m_for_plan, int max_m_hint, hipStream_
     }
     if (debug_enabled())
         std::fprintf(stderr, "[dg] layout=%d rows=%d n=%d k=%d groups=%d cfg=%d (%dx%d, %d waves) tiles=%d grid=%ld units=%d\n",
-                     layout, p.rows, p.n, p.k, p.num_groups, c.id, c.bm, c.bn, c.wm * c.wn, p.num_tiles, grid, units);
+                     layout, p.rows, p.n, p.k, p.num_groups, c.id, c.bm, c.bn, c.wm * c.wn * c.wk, p.num_tiles, grid, units);
     if (c.launch(p, (int)grid, stream) != hipSuccess) {
         (void)hipGetLastError();
         return DG_ERR_HIP;
@@ -413,9 +420,10 @@ int dg_kernel_config_info(int index, int* out) {
     out[1] = cfgs[index].layout;
     out[2] = cfgs[index].bm;
     out[3] = cfgs[index].bn;
-    out[4] = cfgs[index].wm * cfgs[index].wn;
+    out[4] = cfgs[index].wm * cfgs[index].wn * cfgs[index].wk;
     out[5] = cfgs[index].all_formats ? 1 : 0;
     out[6] = cfgs[index].shape_specialised ? 1 : 0;
+    out[7] = cfgs[index].wk;
     return DG_OK;
 }
 

@@ -125,11 +125,20 @@ __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC0
 // NC, KC > 0: an instance for N == NC and K/128 == KC only (tile counts, scale-row
 // offsets, the column guard, loop trip counts and the split into stage groups are
 // then compile-time constants); 0: any N, K.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int NC, int KC>
-__global__ void __launch_bounds__(WM * WN * 64)
+// WK = 2 (dense layout, per-tile loop): the workgroup holds two K groups of WM x WN
+// waves.  Group wk computes the whole tile over the K blocks kb with kb % 2 == wk
+// (each with its own promotion chain, K blocks ascending), so a tile's K loop takes
+// half as many block steps, each step carrying one block per group; at the end of
+// the tile group 0 adds group 1's fp32 sums to its own and stores the tile.  For
+// small-M shapes, whose time is the chain of block steps rather than operand bytes.
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int NC, int KC, int WK>
+__global__ void __launch_bounds__(WM * WN * WK * 64)
 dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const float* __restrict__ sa_ptr,
                const uint8_t* __restrict__ b_ptr, const float* __restrict__ sb_ptr, uint16_t* __restrict__ d_ptr) {
-    constexpr int NW = WM * WN;
+    constexpr int NWG = WM * WN;                   // waves of one K group
+    constexpr int NW = NWG * WK;
+    static_assert(WK == 1 || WK == 2, "one or two K groups");
+    static_assert(WK == 1 || (LAYOUT == kDense && !PIPE), "K groups: dense layout, per-tile loop");
     constexpr int WTM = BM / WM, WTN = BN / WN;
     // operand formats (FMT bit 0: A is E5M2, bit 1: B is E5M2); the MFMA's first
     // source carries B rows and its second A rows.  Field values: 0 = E4M3, 1 = E5M2
@@ -137,11 +146,12 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int NACC = MF * MF / 64;             // accumulator floats per lane per sub-tile
     constexpr int ROWS = BM + BN;
-    // a stage holds the block's operand rows and, behind them, each wave's copy of
-    // the A scales of its rows (64 fp32 values per wave)
-    constexpr int STAGE = ROWS * kKBlock + NW * 256;
+    // a stage holds the operand rows of one K block per K group (SUB bytes each) and,
+    // behind them, each wave's copy of the A scales of its rows (64 fp32 values per wave)
+    constexpr int SUB = ROWS * kKBlock;
+    constexpr int STAGE = WK * SUB + NW * 256;
     constexpr int A_SLOTS = BM / 8, B_SLOTS = BN / 8;
-    constexpr int A_PER = (A_SLOTS + NW - 1) / NW, B_PER = (B_SLOTS + NW - 1) / NW;
+    constexpr int A_PER = (A_SLOTS + NWG - 1) / NWG, B_PER = (B_SLOTS + NWG - 1) / NWG;
     static_assert(MF == 16 || MF == 32, "matrix instruction shape");
     static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "block rows must be a multiple of 8");
@@ -166,10 +176,13 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave % WM, wn = wave / WM;
+    const int wk = WK == 1 ? 0 : wave / NWG;        // K group
+    const int wg = WK == 1 ? wave : wave % NWG;     // wave inside its K group
+    const int wm = wg % WM, wn = wg / WM;
     const int lsub = lane & (MF - 1);             // row of the sub-tile this lane feeds / owns
     const int lgrp = lane / MF;                   // K group of the lane inside an operand fragment
-    const int KB = KC > 0 ? KC : p.kblocks;
+    const int KBT = KC > 0 ? KC : p.kblocks;           // K blocks of the problem
+    const int KB = (KBT + WK - 1) / WK;                // block steps of a tile's K loop
     static_assert((NC > 0) == (KC > 0), "shape instances fix N and K together");
     const int NN = NC > 0 ? NC : p.n;
     const int TILES_N = NC > 0 ? (NC + BN - 1) / BN : p.tiles_n;
@@ -223,12 +236,12 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     uint32_t a_off[A_PER], b_off[B_PER];
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-        const int srow = min(wave + i * NW, A_SLOTS - 1) * 8 + (lane >> 3);
+        const int srow = min(wg + i * NWG, A_SLOTS - 1) * 8 + (lane >> 3);
         a_off[i] = (uint32_t)srow * (uint32_t)p.lda + (uint32_t)((((lane & 7) ^ swz(srow))) * 16);
     }
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
-        const int srow = min(wave + i * NW, B_SLOTS - 1) * 8 + (lane >> 3);
+        const int srow = min(wg + i * NWG, B_SLOTS - 1) * 8 + (lane >> 3);
         b_off[i] = (uint32_t)srow * (uint32_t)p.ldb + (uint32_t)((((lane & 7) ^ swz(BM + srow))) * 16);
     }
     // A scales: a wave's rows of a K block are contiguous in sA (MN-major), so they
@@ -237,7 +250,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // is in the per-lane offset, which the descriptor bounds (rows past the end of
     // sA read zeros).
     const uint32_t sa_voff = (uint32_t)(wm * WTM + lane) * 4u;
-    const int sa_lds = ROWS * kKBlock + wave * 256 + lsub * 4;   // this lane's row, sub-tile 0
+    const int sa_lds = WK * SUB + wave * 256 + lsub * 4;   // this lane's row, sub-tile 0
     // B scale rows a wave reads per K block: MF=16 sub-tiles need at most two (the
     // wave's columns span at most 128); a 128-column wave tile at a multiple of 128
     // needs exactly one, so all of its sub-tiles share one scale product per row
@@ -377,7 +390,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         const int a_rows_read = LAYOUT == kMasked ? valid_rows : p.rows - m0;
         t.rs_a = make_rsrc(a_tile, (long)a_rows_read * p.lda);
         t.rs_b = make_rsrc(b_tile, (long)(NN - n0) * p.ldb);
-        t.rs_sa = make_rsrc(sa_tile, ((long)KB * p.ld_sa - m0) * 4);
+        t.rs_sa = make_rsrc(sa_tile, ((long)KBT * p.ld_sa - m0) * 4);
         // Sub-tile column fn (MF columns, inside one 128-column scale block because MF
         // divides 128 and the column offsets are multiples of MF) reads its B scales
         // from row nb(fn) of sB; the byte offset of that row is wave-uniform.
@@ -387,9 +400,9 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         t.hi_mask = 0;
         if constexpr (MF == 16) {
             const int nb_lo = min(t.wcol0 / kKBlock, NBLK - 1);
-            t.sb_off[0] = nb_lo * KB * 4;
+            t.sb_off[0] = nb_lo * KBT * 4;
             if constexpr (!ONE_SB) {
-                t.sb_off[NSB - 1] = min(nb_lo + 1, NBLK - 1) * KB * 4;
+                t.sb_off[NSB - 1] = min(nb_lo + 1, NBLK - 1) * KBT * 4;
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
                     if ((t.wcol0 + fn * MF) / kKBlock > nb_lo) t.hi_mask |= 1u << fn;
@@ -397,7 +410,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         } else {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                t.sb_off[fn] = min((t.wcol0 + fn * MF) / kKBlock, NBLK - 1) * KB * 4;
+                t.sb_off[fn] = min((t.wcol0 + fn * MF) / kKBlock, NBLK - 1) * KBT * 4;
         }
         t.active = wm * WTM < t.row_hi && wm * WTM + WTM > t.row_lo;
     };
@@ -439,21 +452,30 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     // K = 7168: -12% with the seeded counts, -9% with full groups.  In the dense and
     // contiguous layouts every B and A tile is shared and the hint costs 5-30%.
     constexpr int B_CPOL = LAYOUT == kMasked ? kCpolNT : 0;
+    // With K groups, step kb of the K loop holds K block kb*WK + wk of this wave's group
+    // (its operand rows at sub-block wk of the stage); a block past the last one (K/128
+    // odd) is copied from no memory, i.e. as zeros, and adds nothing.
+    const __amdgpu_buffer_rsrc_t rs_none = make_rsrc(a_ptr, 0);
+    auto kblock = [&](int kb) DG_INLINE { return WK == 1 ? kb : kb * WK + wk; };
     auto issue_slot = [&](const Tile& tl, uint8_t* smem, int kb, int t) DG_INLINE {
-        const int koff = kb * kKBlock;
+        const int kr = kblock(kb);
+        const int koff = kr * kKBlock;
+        uint8_t* const sub = smem + (WK == 1 ? 0 : wk * SUB);
         if (t < A_PER) {
-            const int j = min(wave + t * NW, A_SLOTS - 1);
-            buffer_copy_lds16(tl.rs_a, (lds_void*)(smem + j * 1024), (int)a_off[t], koff);
+            const int j = min(wg + t * NWG, A_SLOTS - 1);
+            buffer_copy_lds16(WK == 1 || kr < KBT ? tl.rs_a : rs_none, (lds_void*)(sub + j * 1024), (int)a_off[t],
+                              koff);
         } else {
-            const int j = min(wave + (t - A_PER) * NW, B_SLOTS - 1);
-            buffer_copy_lds16<B_CPOL>(tl.rs_b, (lds_void*)(smem + BM * kKBlock + j * 1024), (int)b_off[t - A_PER],
-                                      koff);
+            const int j = min(wg + (t - A_PER) * NWG, B_SLOTS - 1);
+            buffer_copy_lds16<B_CPOL>(WK == 1 || kr < KBT ? tl.rs_b : rs_none,
+                                      (lds_void*)(sub + BM * kKBlock + j * 1024), (int)b_off[t - A_PER], koff);
         }
     };
+    // (past the last K block the offset lies outside the tile's sA descriptor: zeros)
     auto issue_sa = [&](const Tile& tl, uint8_t* smem, int kb) DG_INLINE {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(tl.rs_sa,
-                                                 (lds_void*)(smem + ROWS * kKBlock + wave * 256), 4,
-                                                 (int)(sa_voff + (uint32_t)(kb * p.ld_sa) * 4u), 0, 0, 0);
+                                                 (lds_void*)(smem + WK * SUB + wave * 256), 4,
+                                                 (int)(sa_voff + (uint32_t)(kblock(kb) * p.ld_sa) * 4u), 0, 0, 0);
     };
     auto issue_stage = [&](const Tile& tl, uint8_t* smem, int kb) DG_INLINE {
 #pragma unroll
@@ -476,7 +498,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     struct Scales { float a[FM]; float b[NSB]; };
     auto load_sb = [&](const Tile& tl, Scales& sc, int kb) DG_INLINE {
 #pragma unroll
-        for (int t = 0; t < NSB; ++t) sc.b[t] = tl.sb_grp[(tl.sb_off[t] >> 2) + kb];
+        for (int t = 0; t < NSB; ++t) sc.b[t] = tl.sb_grp[(tl.sb_off[t] >> 2) + (WK == 1 ? kb : min(kblock(kb), KBT - 1))];
     };
     auto read_sa = [&](Scales& sc, const uint8_t* smem) DG_INLINE {
 #pragma unroll
@@ -593,7 +615,7 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     v8i bq[RB];                                // B fragment ring (BRING)
     vacc part[R];
     vacc acc[FM][FN];
-    const int arow0 = wm * WTM, bcol0 = BM + wn * WTN;
+    const int arow0 = wk * ROWS + wm * WTM, bcol0 = wk * ROWS + BM + wn * WTN;   // (ROWS is a multiple of 16)
 
     // This lane's byte offsets in a stage from the first row of the wave's A or B
     // rows, made opaque to the compiler so that every fragment read is stage +
@@ -874,7 +896,35 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
         // for each pair of sub-tile columns, two lane-group swaps (V_PERMLANE16_SWAP)
         // give every lane eight adjacent columns of one sub-tile, so a store
         // instruction writes 64 contiguous bytes per row in 16-byte pieces. ----
-        if (cur.active) {
+        if constexpr (WK > 1) {
+            // K groups: group 1 leaves its sums in LDS (stage 0, free once every copy has
+            // landed and every wave has passed the barrier), group 0 adds them to its own
+            constexpr int NV = FM * FN * NACC;       // accumulator floats per lane
+            static_assert(ROWS % 16 == 0, "sub-blocks keep the fragment swizzle");
+            static_assert(NWG * NV * 64 * 4 <= STAGE, "one K group's sums fit a stage");
+            typedef __attribute__((address_space(3))) float lds_f32w;
+            lds_f32w* const red = (lds_f32w*)(lds_u8*)smem0 + wg * NV * 64 + lane;
+            wait_vmem_le<0>();
+            __syncthreads();
+            if (cur.active && wk == 1) {
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int i = 0; i < NACC; ++i) red[((fm * FN + fn) * NACC + i) * 64] = acc[fm][fn][i];
+            }
+            __syncthreads();
+            if (cur.active && wk == 0) {
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int i = 0; i < NACC; ++i) acc[fm][fn][i] += red[((fm * FN + fn) * NACC + i) * 64];
+            }
+        }
+        if (cur.active && wk == 0) {
             auto pack2 = [](float x, float y) DG_INLINE -> uint32_t {
                 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
                 const v2bf t = {(__bf16)x, (__bf16)y};
@@ -951,10 +1001,11 @@ dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const floa
     if constexpr (PIPE) wait_vmem_le<0>();
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int NC = 0, int KC = 0>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int WK, int NC = 0,
+          int KC = 0>
 static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE, FMT, NC, KC>), dim3(grid),
-                       dim3(WM * WN * 64), 0, s, p, p.a, p.sa, p.b, p.sb, p.d);
+    hipLaunchKernelGGL((dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE, FMT, NC, KC, WK>), dim3(grid),
+                       dim3(WM * WN * WK * 64), 0, s, p, p.a, p.sa, p.b, p.sb, p.d);
     return hipGetLastError();
 }
 
@@ -963,7 +1014,7 @@ static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t s) {
 // layout; pipelined (the next tile's first NST blocks run as the tail of the current
 // one) when K/128 splits into whole groups of NST and the configuration fits that
 // variant's registers (PIPE_OK); else the generic per-tile loop.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool SPEC, int FMT>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool SPEC, int FMT, int WK>
 static hipError_t launch_fmt(const GemmParams& p, int grid, hipStream_t s) {
     if constexpr (SPEC) {
         bool done = false;
@@ -973,7 +1024,7 @@ static hipError_t launch_fmt(const GemmParams& p, int grid, hipStream_t s) {
             if constexpr (sh.grouped == (LAYOUT != kDense)) {
                 constexpr bool PIPE = PIPE_OK && sh.kblocks % NST == 0;
                 if (!done && p.n == sh.n && p.kblocks == sh.kblocks) {
-                    e = launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE, FMT, sh.n, sh.kblocks>(p, grid, s);
+                    e = launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE, FMT, WK, sh.n, sh.kblocks>(p, grid, s);
                     done = true;
                 }
             }
@@ -981,44 +1032,45 @@ static hipError_t launch_fmt(const GemmParams& p, int grid, hipStream_t s) {
         if (done) return e;
     }
     if constexpr (PIPE_OK) {
-        if (p.kblocks % NST == 0) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, true, FMT>(p, grid, s);
+        if (p.kblocks % NST == 0) return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, true, FMT, WK>(p, grid, s);
     }
-    return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, FMT>(p, grid, s);
+    return launch_one<BM, BN, WM, WN, LAYOUT, MF, NST, false, FMT, WK>(p, grid, s);
 }
 
 // Configurations with ALL_FMT have instances for the four operand-format pairs (E5M2 on
 // either side); the planner gives the others E4M3 operands only.
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool ALL_FMT, bool SPEC>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, bool ALL_FMT, bool SPEC, int WK>
 static hipError_t launch_cfg(const GemmParams& p, int grid, hipStream_t s) {
     if constexpr (ALL_FMT) {
         switch (p.fmt) {
-            case 1: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 1>(p, grid, s);
-            case 2: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 2>(p, grid, s);
-            case 3: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 3>(p, grid, s);
+            case 1: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 1, WK>(p, grid, s);
+            case 2: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 2, WK>(p, grid, s);
+            case 3: return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 3, WK>(p, grid, s);
             default: break;
         }
     }
     if (p.fmt != 0) return hipErrorInvalidValue;
-    return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 0>(p, grid, s);
+    return launch_fmt<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, SPEC, 0, WK>(p, grid, s);
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK>
+template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE_OK, int WK>
 static hipError_t occupancy_cfg(int* blocks) {
     typedef void (*KernelFn)(const GemmParams, const uint8_t*, const float*, const uint8_t*, const float*, uint16_t*);
-    const KernelFn k0 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, false, 0, 0, 0>;
-    const KernelFn k1 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, 0, 0, 0>;
+    const KernelFn k0 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, false, 0, 0, 0, WK>;
+    const KernelFn k1 = dg_gemm_kernel<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, 0, 0, 0, WK>;
     int b0 = 0, b1 = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, reinterpret_cast<const void*>(k0), WM * WN * 64, 0);
+    constexpr int threads = WM * WN * WK * 64;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, reinterpret_cast<const void*>(k0), threads, 0);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, reinterpret_cast<const void*>(k1), WM * WN * 64, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, reinterpret_cast<const void*>(k1), threads, 0);
     *blocks = b0 < b1 ? b0 : b1;
     return e;
 }
 
-#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF, PIPE_OK, ALL_FMT, SPEC)                               \
-    {ID, LAYOUT, BM, BN, WM, WN, EFF, ALL_FMT, SPEC,                                                            \
-     &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, ALL_FMT, SPEC>,                                      \
-     &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK>},
+#define DG_CFG(ID, LAYOUT, BM, BN, WM, WN, WK, MF, NST, EFF, PIPE_OK, ALL_FMT, SPEC)                           \
+    {ID, LAYOUT, BM, BN, WM, WN, WK, EFF, ALL_FMT, SPEC,                                                        \
+     &launch_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, ALL_FMT, SPEC, WK>,                                  \
+     &occupancy_cfg<BM, BN, WM, WN, LAYOUT, MF, NST, PIPE_OK, WK>},
 
 static const KernelConfig kConfigs[] = {DG_CONFIG_TABLE(DG_CFG)};
 

@@ -32,6 +32,7 @@ struct KernelConfig {
     int id;
     int layout;
     int bm, bn, wm, wn;
+    int wk;                // K groups of waves (1, or 2: each takes every other K block of a tile)
     double eff;            // relative throughput used by the planner
     bool all_formats;      // compiled for E5M2 operands too (else E4M3 only)
     bool shape_specialised;   // has instances for the shapes of kSpecShapes (N and K fixed at compile time)
@@ -52,29 +53,31 @@ constexpr SpecShape kSpecShapes[] = {{false, 7168, 56}, {false, 7168, 16}, {true
 constexpr int kNumSpecShapes = sizeof(kSpecShapes) / sizeof(kSpecShapes[0]);
 
 // The compiled tile configurations: X(id, layout, BLOCK_M, BLOCK_N, waves along M, waves
-// along N, MFMA tile (16 or 32), LDS stages, relative throughput for the planner,
-// pipelined variant fits the registers, E5M2 instances, shape instances).
+// along N, K groups (1, or 2: the K blocks of a tile split between two wave groups whose
+// sums are added at the end), MFMA tile (16 or 32), LDS stages, relative throughput for
+// the planner, pipelined variant fits the registers, E5M2 instances, shape instances).
 // dg_gemm.hip instantiates a kernel for each row; the planner reads the same rows.
 #define DG_CONFIG_TABLE(X)                                                   \
     /* dense */                                                              \
-    X(0, kDense, 256, 224, 4, 2, 16, 2, 1.00, false, false, false)          \
-    X(1, kDense, 256, 224, 8, 1, 32, 2, 0.90, false, false, false)          \
-    X(2, kDense, 128, 128, 2, 2, 16, 4, 0.55, false, false, false)          \
-    X(3, kDense, 64, 112, 4, 1, 16, 4, 0.35, false, true, true)             \
-    X(4, kDense, 128, 224, 4, 2, 16, 3, 0.80, true, false, false)           \
-    X(5, kDense, 256, 256, 4, 2, 16, 2, 1.15, true, true, true)             \
-    X(6, kDense, 64, 64, 4, 1, 16, 4, 0.32, false, true, false)             \
+    X(0, kDense, 256, 224, 4, 2, 1, 16, 2, 1.00, false, false, false)       \
+    X(1, kDense, 256, 224, 8, 1, 1, 32, 2, 0.90, false, false, false)       \
+    X(2, kDense, 128, 128, 2, 2, 1, 16, 4, 0.55, false, false, false)       \
+    X(3, kDense, 64, 112, 4, 1, 1, 16, 4, 0.35, false, true, true)          \
+    X(4, kDense, 128, 224, 4, 2, 1, 16, 3, 0.80, true, false, false)        \
+    X(5, kDense, 256, 256, 4, 2, 1, 16, 2, 1.15, true, true, true)          \
+    X(6, kDense, 64, 64, 4, 1, 1, 16, 4, 0.32, false, true, false)          \
+    X(7, kDense, 64, 64, 4, 1, 2, 16, 4, 0.35, false, false, false)         \
     /* contiguous (BLOCK_M = the 128-row segment alignment, or two of them) */ \
-    X(10, kContiguous, 128, 256, 2, 4, 16, 3, 1.00, false, false, false)    \
-    X(11, kContiguous, 128, 128, 2, 2, 16, 4, 0.55, false, true, false)     \
-    X(12, kContiguous, 128, 256, 2, 4, 16, 2, 0.95, true, false, false)     \
-    X(13, kContiguous, 256, 256, 4, 2, 16, 2, 1.30, false, true, true)      \
+    X(10, kContiguous, 128, 256, 2, 4, 1, 16, 3, 1.00, false, false, false) \
+    X(11, kContiguous, 128, 128, 2, 2, 1, 16, 4, 0.55, false, true, false)  \
+    X(12, kContiguous, 128, 256, 2, 4, 1, 16, 2, 0.95, true, false, false)  \
+    X(13, kContiguous, 256, 256, 4, 2, 1, 16, 2, 1.30, false, true, true)   \
     /* masked */                                                             \
-    X(20, kMasked, 256, 128, 8, 1, 16, 3, 1.00, false, false, false)        \
-    X(21, kMasked, 128, 128, 2, 2, 16, 4, 1.00, false, true, false)         \
-    X(22, kMasked, 256, 128, 4, 2, 16, 3, 0.90, false, false, false)        \
-    X(23, kMasked, 128, 256, 2, 4, 16, 3, 1.15, false, true, false)         \
-    X(24, kMasked, 256, 256, 4, 2, 16, 2, 1.10, false, true, true)
+    X(20, kMasked, 256, 128, 8, 1, 1, 16, 3, 1.00, false, false, false)     \
+    X(21, kMasked, 128, 128, 2, 2, 1, 16, 4, 1.00, false, true, false)      \
+    X(22, kMasked, 256, 128, 4, 2, 1, 16, 3, 0.90, false, false, false)     \
+    X(23, kMasked, 128, 256, 2, 4, 1, 16, 3, 1.15, false, true, false)      \
+    X(24, kMasked, 256, 256, 4, 2, 1, 16, 2, 1.10, false, true, true)
 
 // Table of compiled configurations (defined in dg_gemm.hip).
 const KernelConfig* kernel_configs(int* count);

@@ -19,10 +19,13 @@ extern "C" {
 int dg_set_kernel_config(int config_id);
 
 /* Enumerate the compiled kernel configurations: for index 0, 1, ... fills
- * out[0..6] = config id, layout, block_m, block_n, waves per workgroup, 1 if
- * the configuration also runs E5M2 operands (the _fmt calls) else 0, and 1 if it
+ * out[0..7] = config id, layout, block_m, block_n, waves per workgroup, 1 if
+ * the configuration also runs E5M2 operands (the _fmt calls) else 0, 1 if it
  * has instances compiled for fixed N and K (see dg_describe_launch) else 0, and
- * returns DG_OK; past the last one returns DG_ERR_INVALID_ARG.  Host only. */
+ * the number of K groups (1; 2 where two groups of waves each sum every other K
+ * block of a tile and the two sums are added at the end, which rounds differently
+ * from one chain over all K blocks), and returns DG_OK; past the last one returns
+ * DG_ERR_INVALID_ARG.  out must hold 8 ints.  Host only. */
 int dg_kernel_config_info(int index, int* out);
 
 /* Describe the kernel configuration a call with these sizes would launch, without

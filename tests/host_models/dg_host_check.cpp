@@ -51,9 +51,10 @@ int main() {
     CHECK(dg::g_last_config == 3 && g_last_params.num_tiles == 256 && dg::g_last_grid == 256);
     CHECK(dense(128, 128, 512) == DG_OK);
     CHECK(g_last_params.num_tiles >= 1 && dg::g_last_grid == g_last_params.num_tiles);
-    // small M at K = 7168: 64x64 tiles fill more CUs than 64x112 in the same single round
+    // small M at K = 7168: 64x64 tiles fill more CUs than 64x112 in the same single round, and
+    // with fewer tiles than CUs and a long K the configuration with two K groups of waves
     CHECK(dense(64, 4096, 7168) == DG_OK);
-    CHECK(dg::g_last_config == 6 && g_last_params.num_tiles == 64 && dg::g_last_grid == 64);
+    CHECK(dg::g_last_config == 7 && g_last_params.num_tiles == 64 && dg::g_last_grid == 64);   // K groups
     // ---- dense validation, nothing launched on failure
     const int before = dg::g_launches;
     CHECK(dense(128, 128, 200) == DG_ERR_UNSUPPORTED);                // K % 128
@@ -132,10 +133,10 @@ int main() {
     CHECK(dg_set_kernel_config(999) == DG_ERR_INVALID_ARG);
     CHECK(dg_set_kernel_config(-1) == DG_OK);
     CHECK(dense(4096, 7168, 7168) == DG_OK && dg::g_last_config == 5);
-    int info[7];
+    int info[8];
     int ninfo = 0;
     while (dg_kernel_config_info(ninfo, info) == DG_OK) ++ninfo;
-    CHECK(ninfo == 16);
+    CHECK(ninfo == 17);
 
     // ---- casts and the sA helpers
     const int aux = dg::g_aux_launches;

@@ -32,8 +32,8 @@ hipError_t one_per_cu(int* blocks) {
     return hipSuccess;
 }
 
-#define DG_STUB_CFG(ID, LAYOUT, BM, BN, WM, WN, MF, NST, EFF, PIPE_OK, ALL_FMT, SPEC) \
-    {ID, LAYOUT, BM, BN, WM, WN, EFF, ALL_FMT, SPEC, &record_launch<ID>, &one_per_cu},
+#define DG_STUB_CFG(ID, LAYOUT, BM, BN, WM, WN, WK, MF, NST, EFF, PIPE_OK, ALL_FMT, SPEC) \
+    {ID, LAYOUT, BM, BN, WM, WN, WK, EFF, ALL_FMT, SPEC, &record_launch<ID>, &one_per_cu},
 
 const KernelConfig kStubConfigs[] = {DG_CONFIG_TABLE(DG_STUB_CFG)};
 

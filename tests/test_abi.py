@@ -194,6 +194,25 @@ def test_describe_launch_shapes():
     assert (d["block_m"], d["block_n"], d["grid"]) == (256, 128, 224)
 
 
+def test_describe_launch_k_groups():
+    """Two wave groups over alternate K blocks (k_groups 2) only where the tiles leave
+    CUs idle or just fill them and K is long: 64x4096x7168 (64 tiles of 64x64) and
+    128x7168x7168 (224) take them; the same shapes at K = 2048, or with more tiles than
+    CUs, keep one chain."""
+    groups = {c["id"]: c["k_groups"] for c in dg.dg_kernel_config_info()}
+    assert sorted(set(groups.values())) == [1, 2]
+    assert all(c["layout"] == 0 for c in dg.dg_kernel_config_info() if c["k_groups"] == 2)
+    for m, n, k, want in ((64, 4096, 7168, 2), (128, 7168, 7168, 2), (64, 4096, 4096, 2), (64, 4096, 2048, 1),
+                          (256, 7168, 2048, 1), (512, 4096, 7168, 1), (4096, 7168, 7168, 1)):
+        d = dg.dg_describe_launch(0, m, n, k, 1, 256)
+        assert groups[d["config_id"]] == want, (m, n, k, d)
+        if want == 2:
+            assert d["tiles"] <= 256 and d["waves_per_workgroup"] == 8
+    # a CU cap below the tile count drops them
+    d = dg.dg_describe_launch(0, 128, 7168, 7168, 1, 200)
+    assert groups[d["config_id"]] == 1
+
+
 def test_describe_reports_shape_instances():
     """The V3 shapes run instances compiled for their N and K: dense N = 7168 with
     K = 7168 or 2048, contiguous and masked N = 4096 with K = 7168; another N or K, and

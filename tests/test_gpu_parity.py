@@ -30,6 +30,32 @@ def configs_of(layout):
     return [c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == layout]
 
 
+def k_groups(cfg, m=0, n=0, k=0):
+    """Summation class of a configuration: 1 = one promotion chain over all K blocks
+    (every such configuration gives the same bits), 2 = two wave groups over alternate
+    K blocks whose sums are added at the end (the same bits as each other, not as
+    class 1).  cfg -1 is the planner's pick for a dense m x n x k call."""
+    if cfg == -1:
+        cfg = dg.dg_describe_launch(0, m, n, k, 1)["config_id"]
+    return {c["id"]: c["k_groups"] for c in dg.dg_kernel_config_info()}[cfg]
+
+
+def assert_equal_per_class(outs):
+    """outs: [(summation class, bits)]; the outputs of one class are identical."""
+    first = {}
+    for cls, o in outs:
+        if cls in first:
+            assert np.array_equal(o, first[cls]), f"outputs of summation class {cls} differ"
+        else:
+            first[cls] = o
+
+
+# a dense configuration with one promotion chain, for bit-exact comparisons with the
+# grouped layouts (which sum every K block in one chain)
+def dense_one_chain():
+    return next(c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and c["k_groups"] == 1)
+
+
 def run_dense(dd, cfg=-1, pad_cols=16):
     """GPU dense GEMM into a sentinel-filled buffer wider than N; returns (out bits, full bits)."""
     import torch
@@ -61,9 +87,8 @@ def test_dense_small_workload_all_configs(orc):
         out, full = run_dense(dd, cfg)
         check_values(out, ref, f"dense128 cfg{cfg}")
         assert np.all(full[:, 128:] == W.SENTINEL_BF16)
-        outs.append(out)
-    for o in outs[1:]:
-        assert np.array_equal(o, outs[0])          # identical arithmetic in every tile shape
+        outs.append((k_groups(cfg, 128, 128, 512), out))
+    assert_equal_per_class(outs)                   # identical arithmetic in every tile shape
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (17, 48, 256), (300, 208, 384), (129, 400, 640),
@@ -77,9 +102,8 @@ def test_dense_ragged_shapes(orc, m, n, k):
         out, full = run_dense(dd, cfg)
         check_values(out, ref, f"dense {m}x{n}x{k} cfg{cfg}")
         assert np.all(full[:, n:] == W.SENTINEL_BF16), "wrote past column n"
-        outs.append(out)
-    for o in outs[1:]:
-        assert np.array_equal(o, outs[0])
+        outs.append((k_groups(cfg), out))
+    assert_equal_per_class(outs)
 
 
 @pytest.mark.parametrize("m,n,k", [(300, 400, 640), (64, 7168, 2048)])
@@ -90,8 +114,11 @@ def test_dense_strided_operands(orc, m, n, k):
     import torch
     dd = W.make_dense(m, n, k, seed=m + n + k)
     ref = oracle_dense(orc, dd)
-    packed, _ = run_dense(dd)
-    check_values(packed, ref, f"dense packed {m}x{n}x{k}")
+    packed = {}
+    for cls in (1, 2):
+        cfg = next(c["id"] for c in dg.dg_kernel_config_info() if c["layout"] == 0 and c["k_groups"] == cls)
+        packed[cls], _ = run_dense(dd, cfg)
+        check_values(packed[cls], ref, f"dense packed {m}x{n}x{k} cfg{cfg}")
     lda, ldb, ld_sa, ldd = k + 256, k + 128, dd["sa"].shape[1] + 8, n + 24
     a_buf = torch.zeros((m, lda), dtype=torch.uint8, device="cuda:0")
     b_buf = torch.zeros((n, ldb), dtype=torch.uint8, device="cuda:0")
@@ -110,7 +137,8 @@ def test_dense_strided_operands(orc, m, n, k):
         finally:
             dg.dg_set_kernel_config(-1)
         fb = bits(d_buf)
-        assert np.array_equal(fb[:, :n], packed), f"strided operands changed the result (cfg {cfg})"
+        assert np.array_equal(fb[:, :n], packed[k_groups(cfg, m, n, k)]), \
+            f"strided operands changed the result (cfg {cfg})"
         assert np.all(fb[:, n:] == W.SENTINEL_BF16), "a column between rows was written"
 
 
@@ -187,6 +215,24 @@ def test_dense_shape_instances(orc, k):
         dg.dg_set_num_cus(0)
 
 
+@pytest.mark.parametrize("m,n,k", [(64, 4096, 7168), (128, 2048, 4096)])
+def test_dense_k_groups_planned_full_compare(orc, m, n, k):
+    """Under-filled long-K shapes plan two wave groups over alternate K blocks: the
+    whole output against the oracle, and within the same tolerance of a one-chain
+    configuration's output (the two differ only in how the K blocks' sums are
+    rounded together)."""
+    d = dg.dg_describe_launch(0, m, n, k, 1)
+    assert k_groups(d["config_id"]) == 2, d
+    dd = W.make_dense(m, n, k, seed=m + k)
+    ref = oracle_dense(orc, dd)
+    say(f"dense {m}x{n}x{k} planned cfg={d['config_id']}")
+    out, full = run_dense(dd)
+    assert np.all(full[:, n:] == W.SENTINEL_BF16)
+    check_values(out, ref, f"dense {m}x{n}x{k} k groups")
+    one, _ = run_dense(dd, dense_one_chain())
+    check_values(one, ref, f"dense {m}x{n}x{k} one chain")
+
+
 def test_dense_per_tensor_scaling(orc):
     """Per-tensor scaling is the special case of one value in every scale block: the
     same kernel, checked against the oracle with constant sA and sB."""
@@ -214,7 +260,7 @@ def dense_gpu_segment(cd, g, lo, hi):
     seg = {"a": cd["a"][lo:hi], "sa": np.ascontiguousarray(cd["sa"][:, lo:hi]), "b": cd["b"][g],
            "sb": cd["sb"][g]}
     seg["sa"] = np.pad(seg["sa"], ((0, 0), (0, (-seg["sa"].shape[1]) % 4)))
-    out, _ = run_dense(seg)
+    out, _ = run_dense(seg, dense_one_chain())
     return out
 
 
@@ -380,7 +426,7 @@ def test_masked_edges_all_configs(orc, max_m):
     for g in (1, 3, 5):
         seg = {"a": md["a"][g][:mm[g]], "sa": md["sa"][g][:, :mm[g]], "b": md["b"][g], "sb": md["sb"][g]}
         seg["sa"] = np.pad(seg["sa"], ((0, 0), (0, (-mm[g]) % 4)))
-        dense, _ = run_dense(seg)
+        dense, _ = run_dense(seg, dense_one_chain())
         assert np.array_equal(dense, outs[0][g, :mm[g]])
 
 

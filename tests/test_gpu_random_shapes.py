@@ -69,7 +69,12 @@ def test_dense_random(orc, case):
         assert np.all(fb[:, n:] == W.SENTINEL_BF16), "a column past N was written"
         check_values(fb[:, :n], ref, f"dense {m}x{n}x{k} cfg{c}")
         outs.append(fb)
-    assert np.array_equal(outs[0], outs[1])
+    # bit-identical where both sum every K block in one chain (every configuration but
+    # the K-group ones, which add two partial sums at the end)
+    planned = dg.dg_describe_launch(0, m, n, k, 1, cap)["config_id"]
+    groups = {c["id"]: c["k_groups"] for c in dg.dg_kernel_config_info()}
+    if groups[planned] == groups[cfg]:
+        assert np.array_equal(outs[0], outs[1])
 
 
 @pytest.mark.parametrize("case", range(CASES))
