@@ -66,7 +66,7 @@ constexpr int kNumSpecShapes = sizeof(kSpecShapes) / sizeof(kSpecShapes[0]);
     X(4, kDense, 128, 224, 4, 2, 1, 16, 3, 0.80, true, false, false)        \
     X(5, kDense, 256, 256, 4, 2, 1, 16, 2, 1.15, true, true, true)          \
     X(6, kDense, 64, 64, 4, 1, 1, 16, 4, 0.32, false, true, false)          \
-    X(7, kDense, 64, 64, 4, 1, 2, 16, 4, 0.35, false, false, false)         \
+    X(7, kDense, 64, 64, 4, 1, 2, 16, 4, 0.35, false, true, false)          \
     /* contiguous (BLOCK_M = the 128-row segment alignment, or two of them) */ \
     X(10, kContiguous, 128, 256, 2, 4, 1, 16, 3, 1.00, false, false, false) \
     X(11, kContiguous, 128, 128, 2, 2, 1, 16, 4, 0.55, false, true, false)  \
