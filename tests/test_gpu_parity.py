@@ -233,6 +233,44 @@ def test_dense_k_groups_planned_full_compare(orc, m, n, k):
     check_values(one, ref, f"dense {m}x{n}x{k} one chain")
 
 
+def test_dense_k_groups_deterministic():
+    """The two-K-group configuration adds its groups' sums in a fixed order: the same bits
+    under CU caps (fewer workgroups, more tiles each) and in every replay of a captured
+    HIP graph, with eager work between the replays."""
+    import torch
+    m, n, k = 64, 2048, 4096
+    cfg = dg.dg_describe_launch(0, m, n, k, 1)["config_id"]
+    assert k_groups(cfg) == 2
+    dd = W.make_dense(m, n, k, seed=57)
+    base, _ = run_dense(dd)
+    for cap in (37, 5):
+        dg.dg_set_num_cus(cap)
+        try:
+            say(f"dense {m}x{n}x{k} cfg={cfg}, cu cap {cap}")
+            out, _ = run_dense(dd, cfg)
+        finally:
+            dg.dg_set_num_cus(0)
+        assert np.array_equal(out, base), f"cu cap {cap} changed the bits"
+    dv = upload(dd)
+    d = sentinel_like((m, n))
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):      # warm-up outside capture
+        dg.dg_gemm_fp8_nt(dv["a"], dv["sa"], dv["b"], dv["sb"], d)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dg.dg_gemm_fp8_nt(dv["a"], dv["sa"], dv["b"], dv["sb"], d)
+    for rep in range(3):
+        d.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"dense {m}x{n}x{k} k groups, graph replay {rep}")
+        assert np.array_equal(bits(d), base), f"replay {rep} differs from the eager call"
+
+
 def test_dense_per_tensor_scaling(orc):
     """Per-tensor scaling is the special case of one value in every scale block: the
     same kernel, checked against the oracle with constant sA and sB."""
