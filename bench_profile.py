@@ -290,6 +290,9 @@ def summarize(args) -> int:
         lines.append(f"mean duration, all dispatches: {mean(durs) / 1e3:.2f} us")
         lines.append(f"mean duration, timed window (last {len(win)} dispatches): {mean(win) / 1e3:.2f} us "
                      f"(min {min(win) / 1e3:.2f}, max {max(win) / 1e3:.2f})" if win else "timed window: none")
+        if durs:
+            # in dispatch order: the chip's clock changes show as steps within the run
+            lines.append("durations in dispatch order (us): " + " ".join(f"{d / 1e3:.1f}" for d in durs))
         if bench_us is not None:
             lines.append(f"bench line of the traced run (one HIP event pair over its timed launches): {bench_us:.2f} us")
             lines.append("  (the trace adds a few us of dispatch overhead between launches, which the bench line "
