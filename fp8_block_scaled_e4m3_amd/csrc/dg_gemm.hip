@@ -130,7 +130,8 @@ __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC0
 // (each with its own promotion chain, K blocks ascending), so a tile's K loop takes
 // half as many block steps, each step carrying one block per group; at the end of
 // the tile group 0 adds group 1's fp32 sums to its own and stores the tile.  For
-// small-M shapes, whose time is the chain of block steps rather than operand bytes.
+// small-M shapes with long K whose tiles leave CUs idle: there a tile's time is its
+// chain of block steps, not the CU's share of the operand bytes.
 template <int BM, int BN, int WM, int WN, int LAYOUT, int MF, int NST, bool PIPE, int FMT, int NC, int KC, int WK>
 __global__ void __launch_bounds__(WM * WN * WK * 64)
 dg_gemm_kernel(const GemmParams p, const uint8_t* __restrict__ a_ptr, const float* __restrict__ sa_ptr,
