@@ -18,6 +18,10 @@
  * Each K block's partial product is multiplied by sA*sB and added into an fp32
  * accumulator, K blocks in ascending order (the README's two-level "promotion";
  * the per-1x128 / per-128x128 granularity is DeepSeek-V3's fine-grained scheme).
+ * One exception, dense calls only: where the tiles leave CUs idle and K/128 >= 32
+ * (few rows, long K), the even and the odd K blocks are summed in two such chains
+ * whose fp32 sums are added at the end; the result then agrees with the one-chain
+ * result to fp32 rounding but need not be bit-identical to it.
  *
  * Conventions for every entry point:
  *  - Pointers named a, sa, b, sb, d, m_indices, masked_m are DEVICE pointers owned by
